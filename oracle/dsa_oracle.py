@@ -1,0 +1,398 @@
+"""Plain CPU oracle for DeepSeek-style sparse attention (DSA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports, links or calls this
+module; only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may use it.  It shares no code with the HIP path.
+
+Everything is computed in numpy float64, one query row at a time, in the order
+and notation of the pages:
+
+  * lightning-indexer score: for query i and key j,
+        s(i, j) = sum_h w(i, h) * max(0, q(i, h) . k(j))
+    the ReLU is applied to each head's dot product *before* the weighted head
+    sum (llama.cpp mirror commit c88c916636, last paragraph: the fix that moved
+    the index Jaccard from 0.794 to 0.975; ik_llama.cpp PR #2058, first commit
+    "lightning indexer ... batch-local": relu of the key/query product, scaled
+    per-head weights, head sum, causal mask, top-k of min(top_k, n_tokens));
+  * the causal mask: key j is visible to query i iff j <= pos(i) (and j is a
+    stored row of the query's own sequence);
+  * top-k: the k highest visible scores, k = min(top_k, n_visible);
+  * attention-sink force-include: the first n_sink keys of the query's own
+    sequence are always kept (PR #2058, "UPDATE 5" commit: per-sequence sink
+    boost of 1e20 on the sequence's first positions);
+  * block-pooled ("QSA") selection: one mean-pooled raw key per complete block
+    of c positions, the best top_k / c blocks, plus the incomplete tail
+    (llama.cpp mirror commit c88c916636, first to fourth paragraphs);
+  * attention over the selected keys only, softmax in two passes (max, then
+    exp-sum); dense causal attention is a separate function (PR #2058: the
+    indexer is an exact no-op when top_k >= n_tokens);
+  * the orthonormal Sylvester Walsh-Hadamard rotation of indexer q and k
+    ((Hq).(Hk) = q.k, H symmetric with H.H = I: PR #2058 first and
+    "kr_l maintenance" commits).
+
+Where the pages leave a step open, the reading taken is stated at the function
+that takes it.  Every function is pinned by tests in tests/test_oracle.py
+against brute force, closed forms, library routines or invariants the pages
+fix; the page-level accuracy figures (Jaccard 0.975 against vLLM, perplexity
+equalities on GLM-5.2) need trained weights and datasets and are not
+reproduced: parity unpinned for those figures, which no function here claims.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+# --------------------------------------------------------------------------
+# Exact decoding of stored element types into float64.
+# --------------------------------------------------------------------------
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly.
+
+    A bf16 value is the upper half of an IEEE binary32 word.
+    """
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64, exactly."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_fp8_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP float8 e4m3fn codes (uint8) -> float64, exactly.
+
+    Layout: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent 0
+    is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN; there is no
+    infinity, so 0x7E = 448 is the largest finite value.  The format is not on
+    the pages: it is the stored index-key type of the long-decode workload.
+    """
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.power(2.0, (e - 7).astype(np.float64))
+    sub = (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 15) & ((b & 0x7) == 7), np.nan, val)
+    return sign * val
+
+
+def to_f64(t) -> np.ndarray:
+    """A torch tensor (f32/f64/bf16/f16/float8_e4m3fn) -> float64 numpy array.
+
+    bf16, f16 and fp8 are decoded from their bit patterns by the functions
+    above; f32/f64 are widened by numpy.
+    """
+    import torch  # local: the oracle's arithmetic does not depend on torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return decode_bf16(t.view(torch.int16).numpy().view(np.uint16))
+    if t.dtype == torch.float16:
+        return decode_f16(t.view(torch.int16).numpy().view(np.uint16))
+    if t.dtype == torch.float8_e4m3fn:
+        return decode_fp8_e4m3fn(t.view(torch.uint8).numpy())
+    if t.dtype in (torch.float32, torch.float64):
+        return t.numpy().astype(np.float64)
+    if t.dtype in (torch.int32, torch.int64):
+        return t.numpy().astype(np.int64)
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotation.
+# --------------------------------------------------------------------------
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Normalised Sylvester Hadamard matrix of order n (a power of two).
+
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], scaled by 1/sqrt(n) so that H
+    is orthonormal and symmetric (H.H = I), natural (Sylvester) order.
+    (ik_llama.cpp PR #2058, "kr_l maintenance" commit: the same Sylvester
+    construction fills the rotation; un-rotating is a second application.)
+    """
+    if n < 1 or n & (n - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / math.sqrt(n)
+
+
+# --------------------------------------------------------------------------
+# Visibility.
+# --------------------------------------------------------------------------
+
+
+def visible_tokens(q_pos: int, kv_len: int) -> int:
+    """Number of visible token keys of a query: keys 0 .. n-1.
+
+    Key j (cache row j of the query's own sequence, at position j) is visible
+    iff j <= q_pos and j < kv_len (causal mask; sequences never see each
+    other).  q_pos < 0 sees nothing.
+    """
+    return max(0, min(q_pos + 1, kv_len))
+
+
+def complete_blocks(q_pos: int, kv_len: int, c: int) -> int:
+    """Number of complete blocks of c positions visible to a query.
+
+    Reading: a block [b*c, b*c + c) counts as complete for query i iff its last
+    position b*c + c - 1 is visible to i (<= q_pos and < kv_len).  Blocks are
+    cuts of the position line starting at the sequence's first position
+    (llama.cpp mirror commit c88c916636, fourth paragraph).
+    """
+    return visible_tokens(q_pos, kv_len) // c
+
+
+# --------------------------------------------------------------------------
+# S0/S2: lightning-indexer scores.
+# --------------------------------------------------------------------------
+
+
+def index_scores_row(q: np.ndarray, w: np.ndarray, keys: np.ndarray,
+                     n_vis: int, key_scale: Optional[np.ndarray] = None,
+                     rotate_q: bool = False) -> np.ndarray:
+    """Scores of one query row against all units of its sequence.
+
+    q [H, D], w [H], keys [n_units, D] (token keys, or pooled block keys),
+    key_scale [n_units] (per-row dequantisation scale, or None).
+    Returns s [n_units]: s(u) = sum_h w(h) * max(0, q'(h) . k(u)) for the first
+    n_vis units, -inf for the rest, where k(u) = keys(u) * key_scale(u) and
+    q' = H q if rotate_q (keys then hold H k, so q'.Hk = q.k).
+
+    No extra scale is applied: any softmax scale of the indexer is taken to be
+    folded into w by the caller (the pages call the weights "scaled" without
+    giving the scale).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if rotate_q:
+        q = q @ hadamard(q.shape[-1]).T
+    k = np.asarray(keys[:n_vis], dtype=np.float64)
+    if key_scale is not None:
+        k = k * np.asarray(key_scale[:n_vis], dtype=np.float64)[:, None]
+    out = np.full(keys.shape[0], NEG_INF)
+    if n_vis > 0:
+        dots = q @ k.T                       # [H, n_vis], one dot per head
+        out[:n_vis] = (np.asarray(w, dtype=np.float64)[:, None] *
+                       np.maximum(dots, 0.0)).sum(axis=0)
+    return out
+
+
+def index_scores(q, k, w, q_pos, kv_len=None, c: int = 1, k_scale=None,
+                 rotate_q: bool = False, rows: Optional[Sequence] = None):
+    """Indexer scores for a batch.
+
+    q [S, n_q, H, D], k [S, n_units, D] (token keys if c == 1, pooled block
+    keys if c > 1), w [S, n_q, H], q_pos [S, n_q] int, kv_len [S] or None
+    (= n_units * c), k_scale [S, n_units] or None.
+    rows: optional list of (s, i) to compute; default all.
+    Returns a float64 array [S, n_q, n_units] (rows not asked for are NaN).
+    """
+    S, n_q = q.shape[0], q.shape[1]
+    n_units = k.shape[1]
+    if kv_len is None:
+        kv_len = [n_units * c] * S
+    out = np.full((S, n_q, n_units), np.nan)
+    todo = rows if rows is not None else [(s, i) for s in range(S) for i in range(n_q)]
+    for s, i in todo:
+        nv = visible_tokens(int(q_pos[s][i]), int(kv_len[s]))
+        if c > 1:
+            nv = nv // c
+        out[s, i] = index_scores_row(q[s, i], w[s, i], k[s], nv,
+                                     None if k_scale is None else k_scale[s],
+                                     rotate_q)
+    return out
+
+
+# --------------------------------------------------------------------------
+# S3: top-k selection.
+# --------------------------------------------------------------------------
+
+
+def topk_row(scores: np.ndarray, n_vis: int, k: int, n_sink: int = 0) -> np.ndarray:
+    """Ascending indices of the units selected for one query row.
+
+    K = min(k, n_vis) units are kept among the visible units 0 .. n_vis-1:
+    first the forced sinks {j < n_sink}, then the K - |forced| best remaining
+    units by (score descending, index ascending).
+
+    Readings: k counts per query after the causal mask (the pages'
+    min(top_k, n_tokens) with masked keys at -inf); ties at the k-th score go
+    to the lowest index; the sink keys are forced in rather than boosted by
+    1e20, which is the same set whenever n_sink <= K; the output is a set,
+    emitted in ascending order.
+    """
+    K = min(k, n_vis)
+    forced = np.arange(min(n_sink, n_vis), dtype=np.int64)
+    rest = K - forced.size
+    cand = np.arange(forced.size, n_vis, dtype=np.int64)
+    if rest > 0 and cand.size > 0:
+        vals = np.asarray(scores[forced.size:n_vis], dtype=np.float64)
+        order = np.lexsort((cand, -vals))   # primary: score desc; then index asc
+        chosen = cand[order[:rest]]
+    else:
+        chosen = np.zeros(0, dtype=np.int64)
+    return np.sort(np.concatenate([forced, chosen]))
+
+
+def topk(scores, q_pos, k_out: int, kv_len=None, c: int = 1, n_sink: int = 0,
+         rows: Optional[Sequence] = None):
+    """Top-k for a batch of score rows [S, n_q, n_units].
+
+    Returns int64 [S, n_q, k_out]: selected unit ids ascending, -1 padded.
+    With c > 1 the units are complete blocks and k_out = top_k / c.
+    """
+    S, n_q, n_units = scores.shape
+    if kv_len is None:
+        kv_len = [n_units * c] * S
+    out = np.full((S, n_q, k_out), -1, dtype=np.int64)
+    todo = rows if rows is not None else [(s, i) for s in range(S) for i in range(n_q)]
+    for s, i in todo:
+        nv = visible_tokens(int(q_pos[s][i]), int(kv_len[s]))
+        if c > 1:
+            nv = nv // c
+        sel = topk_row(scores[s, i], nv, k_out, n_sink if c == 1 else 0)
+        out[s, i, :sel.size] = sel
+    return out
+
+
+# --------------------------------------------------------------------------
+# S1/S4: block pooling and block-mode token sets.
+# --------------------------------------------------------------------------
+
+
+def block_pool(k_raw: np.ndarray, c: int) -> np.ndarray:
+    """Mean of every complete block of c raw key rows.
+
+    k_raw [S, n_kv, D] -> [S, n_kv // c, D]; block b = rows b*c .. b*c + c - 1.
+    Pooling happens on the raw (un-normed, un-rotated) keys (llama.cpp mirror
+    commit c88c916636, second paragraph).  Any post-pool norm or rotation
+    carries model weights and is outside this path: the pooled key is scored
+    as is.
+    """
+    S, n_kv, D = k_raw.shape
+    nb = n_kv // c
+    out = np.zeros((S, nb, D))
+    for b in range(nb):
+        out[:, b, :] = np.asarray(k_raw[:, b * c:(b + 1) * c, :], dtype=np.float64).sum(axis=1) / c
+    return out
+
+
+def block_token_set(blocks: np.ndarray, c: int, q_pos: int, kv_len: int) -> np.ndarray:
+    """Tokens attended by a query in block mode, in attention order.
+
+    The live selected blocks (ids >= 0), each expanded to its c positions in
+    list order, followed by the incomplete tail n_cb*c .. n_vis-1.  The tail
+    does not count against the block budget; with it the selection is dense
+    below top_k + c - 1 cached tokens (llama.cpp mirror commit c88c916636,
+    first paragraph).
+    """
+    n_vis = visible_tokens(q_pos, kv_len)
+    n_cb = n_vis // c
+    toks = [np.arange(b * c, b * c + c) for b in blocks if 0 <= b < n_cb]
+    toks.append(np.arange(n_cb * c, n_vis))
+    return np.concatenate(toks).astype(np.int64) if toks else np.zeros(0, np.int64)
+
+
+def token_list(idx_row: np.ndarray, q_pos: int, kv_len: int) -> np.ndarray:
+    """Tokens attended in token mode: the live entries of an index row in list
+    order (-1 entries and invisible ids are dropped)."""
+    n_vis = visible_tokens(q_pos, kv_len)
+    idx_row = np.asarray(idx_row, dtype=np.int64)
+    return idx_row[(idx_row >= 0) & (idx_row < n_vis)]
+
+
+# --------------------------------------------------------------------------
+# S5: attention over a token set; dense causal attention.
+# --------------------------------------------------------------------------
+
+
+def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, tokens: np.ndarray,
+           scale: float) -> np.ndarray:
+    """Softmax attention of one query over the listed tokens.
+
+    Q [Hq, Dk], K [n_kv, Hkv, Dk], V [n_kv, Hkv, Dv]; head h reads KV group
+    g = h // (Hq / Hkv) (contiguous grouping).  For each head:
+        l_j = scale * Q(h) . K(j, g),  p_j = exp(l_j - max l) / sum exp(l - max l),
+        o = sum_j p_j V(j, g).
+    An empty token set gives a zero row.  Returns [Hq, Dv].
+    """
+    Hq = Q.shape[0]
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((Hq, V.shape[2]))
+    if tokens.size == 0:
+        return out
+    for g in range(Hkv):
+        kk = np.asarray(K[tokens, g, :], dtype=np.float64)      # [n, Dk]
+        vv = np.asarray(V[tokens, g, :], dtype=np.float64)      # [n, Dv]
+        qg = np.asarray(Q[g * G:(g + 1) * G], dtype=np.float64)  # heads of group g
+        logits = scale * (qg @ kk.T)                             # [G, n]
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        out[g * G:(g + 1) * G] = (p @ vv) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def sparse_attention(Q, K, V, idx, q_pos, kv_len=None, c: int = 1,
+                     scale: Optional[float] = None, rows: Optional[Sequence] = None):
+    """Attention of every query over its selected tokens.
+
+    Q [S, n_q, Hq, Dk], K [S, n_kv, Hkv, Dk], V [S, n_kv, Hkv, Dv],
+    idx [S, n_q, n_sel] int (token ids if c == 1, block ids if c > 1; -1 dead)
+    or None for dense causal attention over all visible keys.
+    Returns float64 [S, n_q, Hq, Dv] (rows not asked for are NaN).
+    """
+    S, n_q, Hq, Dk = Q.shape
+    n_kv = K.shape[1]
+    if kv_len is None:
+        kv_len = [n_kv] * S
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    out = np.full((S, n_q, Hq, V.shape[3]), np.nan)
+    todo = rows if rows is not None else [(s, i) for s in range(S) for i in range(n_q)]
+    for s, i in todo:
+        qp, kl = int(q_pos[s][i]), int(kv_len[s])
+        if idx is None:
+            toks = np.arange(visible_tokens(qp, kl), dtype=np.int64)
+        elif c > 1:
+            toks = block_token_set(idx[s, i], c, qp, kl)
+        else:
+            toks = token_list(idx[s, i], qp, kl)
+        out[s, i] = attend(Q[s, i], K[s], V[s], toks, scale)
+    return out
+
+
+def dense_attention(Q, K, V, q_pos, kv_len=None, scale=None, rows=None):
+    """Dense causal attention: every visible key, in position order."""
+    return sparse_attention(Q, K, V, None, q_pos, kv_len, 1, scale, rows)
+
+
+# --------------------------------------------------------------------------
+# Whole path.
+# --------------------------------------------------------------------------
+
+
+def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
+            k_scale=None, n_sink: int = 0, scale=None, rotate_q: bool = False,
+            rows: Optional[Sequence] = None):
+    """S1 (block mode) -> S2 -> S3 -> S4/S5 for a batch.
+
+    k_idx holds token keys (c == 1) or raw keys that are pooled first (c > 1).
+    Returns (O [S, n_q, Hq, Dv], idx [S, n_q, top_k // c], scores).
+    """
+    units = block_pool(k_idx, c) if c > 1 else k_idx
+    scores = index_scores(q_idx, units, w, q_pos, kv_len, c, k_scale, rotate_q, rows)
+    idx = topk(scores, q_pos, top_k // c, kv_len, c, n_sink, rows)
+    O = sparse_attention(Q, K, V, idx, q_pos, kv_len, c, scale, rows)
+    return O, idx, scores

@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Brute force on tiny inputs, closed forms, library routines (numpy/torch on the
+CPU) and invariants the pages fix.  Each test is chosen so that a plausible
+mistake in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, ReLU after instead of before the head sum, a wrong tie rule or head
+grouping) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoding --
+
+def test_fp8_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_fp8_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # closed-form spot values of the e4m3fn encoding
+    assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    assert ours[0x38] == 1.0 and ours[0xB8] == -1.0
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_16bit_decode_matches_torch_all_patterns(kind):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if kind == "bf16":
+        ours = O.decode_bf16(bits)
+        ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    else:
+        ours = O.decode_f16(bits)
+        ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------- Hadamard --
+
+def test_hadamard_closed_form_and_involution():
+    n = 128
+    H = O.hadamard(n)
+    i = np.arange(n)
+    pop = np.vectorize(lambda x: bin(x).count("1"))(i[:, None] & i[None, :])
+    closed = np.where(pop % 2 == 0, 1.0, -1.0) / math.sqrt(n)
+    assert np.array_equal(H, closed)                      # Sylvester entries
+    assert np.allclose(H @ H, np.eye(n), atol=1e-14, rtol=0)   # H.H = I
+    assert np.array_equal(H, H.T)
+    with pytest.raises(ValueError):
+        O.hadamard(96)
+
+
+# ------------------------------------------------------------------ scores --
+
+def _brute_scores(q, k, w, q_pos, kv_len, key_scale=None):
+    """Scalar loops, written independently of the vectorised oracle."""
+    S, n_q, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    n_k = len(k[0])
+    out = [[[-math.inf] * n_k for _ in range(n_q)] for _ in range(S)]
+    for s in range(S):
+        for i in range(n_q):
+            for j in range(n_k):
+                if j > q_pos[s][i] or j >= kv_len[s]:
+                    continue
+                tot = 0.0
+                for h in range(H):
+                    dot = 0.0
+                    for d in range(D):
+                        kv = k[s][j][d] * (key_scale[s][j] if key_scale is not None else 1.0)
+                        dot += q[s][i][h][d] * kv
+                    if dot > 0.0:
+                        tot += w[s][i][h] * dot
+                out[s][i][j] = tot
+    return np.array(out)
+
+
+def test_scores_match_scalar_brute_force():
+    rng = np.random.default_rng(0)
+    S, n_q, H, D, n_k = 2, 5, 3, 8, 7
+    q = rng.standard_normal((S, n_q, H, D))
+    k = rng.standard_normal((S, n_k, D))
+    w = rng.standard_normal((S, n_q, H))
+    ks = rng.uniform(0.5, 2.0, (S, n_k))
+    q_pos = np.array([[0, 2, 3, 6, 9], [-1, 1, 4, 5, 6]])
+    kv_len = [7, 5]
+    ours = O.index_scores(q, k, w, q_pos, kv_len, 1, ks)
+    ref = _brute_scores(q.tolist(), k.tolist(), w.tolist(), q_pos.tolist(), kv_len, ks.tolist())
+    assert np.array_equal(np.isinf(ours), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(ours[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_scores_relu_before_head_sum_golden():
+    g = json.load(open(os.path.join(GOLDEN, "relu_before_head_sum.json")))
+    s = O.index_scores(np.array(g["q"]), np.array(g["k"]), np.array(g["w"]),
+                       np.array(g["q_pos"]))
+    assert np.array_equal(s, np.array(g["expected_scores"]))
+    idx = O.topk(s, np.array(g["q_pos"]), 1)
+    assert idx.tolist() == g["expected_top1"]
+
+
+def test_scores_single_head_reduce_to_relu_matmul():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 6, 1, 16))
+    k = rng.standard_normal((1, 9, 16))
+    s = O.index_scores(q, k, np.ones((1, 6, 1)), np.full((1, 6), 100))
+    ref = torch.relu(torch.from_numpy(q[0, :, 0]) @ torch.from_numpy(k[0]).T).numpy()
+    assert np.allclose(s[0], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_scores_invariant_under_hadamard_rotation():
+    rng = np.random.default_rng(2)
+    D = 128
+    q = rng.standard_normal((2, 3, 4, D))
+    k = rng.standard_normal((2, 50, D))
+    w = rng.standard_normal((2, 3, 4))
+    qp = np.array([[10, 30, 49], [0, 25, 60]])
+    H = O.hadamard(D)
+    plain = O.index_scores(q, k, w, qp)
+    rotated = O.index_scores(q, k @ H.T, w, qp, rotate_q=True)
+    fin = np.isfinite(plain)
+    assert np.array_equal(fin, np.isfinite(rotated))
+    assert np.allclose(plain[fin], rotated[fin], rtol=1e-12, atol=1e-10)
+    # rotating only one side does change the scores
+    one_side = O.index_scores(q, k @ H.T, w, qp)
+    assert not np.allclose(plain[fin], one_side[fin], rtol=1e-3)
+
+
+def test_scores_homogeneous_in_key_scale_and_linear_in_w():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 32))
+    k = rng.standard_normal((20, 32))
+    w1, w2 = rng.standard_normal(4), rng.standard_normal(4)
+    a = rng.uniform(0.1, 5.0, 20)
+    base = O.index_scores_row(q, w1, k, 20)
+    assert np.allclose(O.index_scores_row(q, w1, k, 20, key_scale=a), a * base, rtol=1e-12)
+    s12 = O.index_scores_row(q, w1 + w2, k, 20)
+    assert np.allclose(s12, base + O.index_scores_row(q, w2, k, 20), rtol=1e-11, atol=1e-11)
+    # a negative key scale is not homogeneous: the ReLU sees the sign
+    assert not np.allclose(O.index_scores_row(q, w1, -k, 20), -base)
+
+
+def test_scores_visibility():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 3, 2, 8))
+    k = rng.standard_normal((1, 10, 8))
+    w = np.abs(rng.standard_normal((1, 3, 2))) + 0.1
+    s = O.index_scores(q, k, w, np.array([[-1, 3, 20]]), kv_len=[6])
+    assert np.all(np.isneginf(s[0, 0]))
+    assert np.all(np.isfinite(s[0, 1, :4])) and np.all(np.isneginf(s[0, 1, 4:]))
+    assert np.all(np.isfinite(s[0, 2, :6])) and np.all(np.isneginf(s[0, 2, 6:]))
+    # block units: block b visible iff its last position is visible
+    sb = O.index_scores(q, k[:, :5], w, np.array([[6, 7, 9]]), kv_len=[10], c=2)
+    assert np.isfinite(sb[0, 0]).sum() == 3 and np.isfinite(sb[0, 1]).sum() == 4
+    assert np.isfinite(sb[0, 2]).sum() == 5
+
+
+# ------------------------------------------------------------------- top-k --
+
+def test_topk_maximises_sum_by_brute_force():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 12))
+        sc = rng.standard_normal(n)
+        sel = O.topk_row(sc, n, k)
+        K = min(k, n)
+        best = max(itertools.combinations(range(n), K), key=lambda c: sum(sc[list(c)]))
+        assert sel.tolist() == sorted(best)
+
+
+def test_topk_matches_torch_topk_on_distinct_scores():
+    rng = np.random.default_rng(6)
+    sc = rng.standard_normal(5000)
+    sel = O.topk_row(sc, 4000, 777)
+    ref = torch.topk(torch.from_numpy(sc[:4000]), 777).indices.sort().values.numpy()
+    assert np.array_equal(sel, ref)
+
+
+def test_topk_ties_go_to_lowest_index():
+    assert O.topk_row(np.zeros(50), 50, 7).tolist() == list(range(7))
+    sc = np.array([1.0, 5.0, 3.0, 5.0, 3.0, 3.0, 0.0])
+    assert O.topk_row(sc, 7, 3).tolist() == [1, 2, 3]
+    assert O.topk_row(sc, 7, 4).tolist() == [1, 2, 3, 4]
+
+
+def test_topk_short_rows_keep_everything_and_pad():
+    sc = np.array([[[0.3, -2.0, 1.0, 7.0, -np.inf, -np.inf]]])
+    idx = O.topk(sc, np.array([[3]]), 5)
+    assert idx.tolist() == [[[0, 1, 2, 3, -1]]]
+    idx = O.topk(sc, np.array([[-1]]), 5)
+    assert idx.tolist() == [[[-1] * 5]]
+
+
+def test_topk_sink_is_forced():
+    sc = np.array([-100.0, 5.0, 4.0, 3.0, 2.0, 1.0])
+    assert O.topk_row(sc, 6, 3, n_sink=1).tolist() == [0, 1, 2]
+    assert O.topk_row(sc, 6, 3, n_sink=2).tolist() == [0, 1, 2]
+    sc2 = np.array([-100.0, -50.0, 4.0, 3.0, 2.0, 1.0])
+    assert O.topk_row(sc2, 6, 3, n_sink=2).tolist() == [0, 1, 2]
+    assert O.topk_row(sc2, 6, 3, n_sink=0).tolist() == [2, 3, 4]
+    # the sink equals a +1e20 boost of the first keys when n_sink <= k
+    boosted = sc2.copy()
+    boosted[:2] += 1e20
+    assert O.topk_row(boosted, 6, 3).tolist() == O.topk_row(sc2, 6, 3, n_sink=2).tolist()
+
+
+def test_topk_rows_are_independent():
+    rng = np.random.default_rng(7)
+    sc = rng.standard_normal((3, 4, 40))
+    qp = rng.integers(-1, 45, (3, 4))
+    kv = [40, 33, 12]
+    batched = O.topk(sc, qp, 9, kv, n_sink=1)
+    for s in range(3):
+        alone = O.topk(sc[s:s + 1], qp[s:s + 1], 9, [kv[s]], n_sink=1)
+        assert np.array_equal(alone[0], batched[s])
+
+
+# -------------------------------------------------------------- block mode --
+
+def test_block_pool_against_numpy_mean_and_constants():
+    rng = np.random.default_rng(8)
+    kr = rng.standard_normal((2, 37, 16))
+    p = O.block_pool(kr, 8)
+    assert p.shape == (2, 4, 16)
+    ref = kr[:, :32].reshape(2, 4, 8, 16).mean(axis=2)
+    assert np.allclose(p, ref, rtol=1e-14, atol=1e-15)
+    const = np.broadcast_to(np.arange(5.0)[None, :, None], (1, 5, 3)).repeat(4, axis=1)
+    assert np.array_equal(O.block_pool(const, 4)[0, :, 0], np.arange(5.0))
+    assert np.array_equal(O.block_pool(kr, 1), kr)
+
+
+def _block_case(n_vis, top_k, c, seed=9, H=4, D=16):
+    rng = np.random.default_rng(seed)
+    n_kv = n_vis + 5
+    q = rng.standard_normal((1, 1, H, D))
+    kr = rng.standard_normal((1, n_kv, D))
+    w = rng.standard_normal((1, 1, H))
+    qp = np.array([[n_vis - 1]])
+    pooled = O.block_pool(kr, c)
+    s = O.index_scores(q, pooled, w, qp, kv_len=[n_kv], c=c)
+    blocks = O.topk(s, qp, top_k // c, kv_len=[n_kv], c=c)
+    toks = O.block_token_set(blocks[0, 0], c, n_vis - 1, n_kv)
+    return s, blocks, toks
+
+
+@pytest.mark.parametrize("c,top_k", [(4, 8), (16, 64), (64, 256)])
+def test_block_mode_dense_threshold(c, top_k):
+    # exactly dense below top_k + c - 1 cached tokens ...
+    n = top_k + c - 1
+    _, _, toks = _block_case(n, top_k, c)
+    assert sorted(toks.tolist()) == list(range(n))
+    # ... and the first sparse length drops a whole block
+    n = top_k + c
+    _, blocks, toks = _block_case(n, top_k, c)
+    assert len(toks) == n - c
+    assert (blocks[0, 0] >= 0).sum() == top_k // c
+
+
+def test_block_mode_cuts_on_block_boundaries_and_matches_token_expansion():
+    c, top_k = 8, 24
+    for seed in range(10):
+        n_vis = 93
+        s, blocks, toks = _block_case(n_vis, top_k, c, seed=seed)
+        n_cb = n_vis // c
+        tail = set(range(n_cb * c, n_vis))
+        chosen = set(int(b) for b in blocks[0, 0] if b >= 0)
+        body = set(toks.tolist()) - tail
+        assert body == {b * c + t for b in chosen for t in range(c)}
+        # second, independent path: give every token its block's score, take the
+        # token top-(B*c) (block members tie, the budget is a whole number of
+        # blocks, so the cut lands on a block boundary)
+        tok_scores = np.repeat(s[0, 0, :n_cb], c)
+        tsel = O.topk_row(tok_scores, n_cb * c, top_k)
+        assert set(tsel.tolist()) == body
+
+
+def test_block_mode_c1_is_token_mode():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 3, 2, 8))
+    k = rng.standard_normal((1, 20, 8))
+    w = rng.standard_normal((1, 3, 2))
+    qp = np.array([[5, 12, 19]])
+    s1 = O.index_scores(q, O.block_pool(k, 1), w, qp, c=1)
+    assert np.array_equal(s1, O.index_scores(q, k, w, qp))
+    idx = O.topk(s1, qp, 4)
+    for i in range(3):
+        a = O.block_token_set(idx[0, i], 1, int(qp[0, i]), 20)
+        b = O.token_list(idx[0, i], int(qp[0, i]), 20)
+        assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------- attention --
+
+def _sdpa_ref(Q, K, V, q_pos, kv_len, scale):
+    """torch scaled_dot_product_attention on the CPU in fp64, explicit mask."""
+    S, n_q, Hq, Dk = Q.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((S, n_q, Hq, V.shape[3]))
+    for s in range(S):
+        q = torch.from_numpy(Q[s]).permute(1, 0, 2)                    # [Hq, n_q, Dk]
+        k = torch.from_numpy(K[s]).permute(1, 0, 2).repeat_interleave(G, 0)
+        v = torch.from_numpy(V[s]).permute(1, 0, 2).repeat_interleave(G, 0)
+        j = torch.arange(K.shape[1])
+        mask = (j[None, :] <= torch.from_numpy(q_pos[s])[:, None]) & (j[None, :] < kv_len[s])
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask,
+                                                             scale=scale)
+        out[s] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+def test_dense_attention_matches_torch_sdpa_gqa():
+    rng = np.random.default_rng(11)
+    S, n_q, n_kv, Hq, Hkv, D = 2, 6, 15, 8, 2, 16
+    Q = rng.standard_normal((S, n_q, Hq, D))
+    K = rng.standard_normal((S, n_kv, Hkv, D))
+    V = rng.standard_normal((S, n_kv, Hkv, 12))
+    qp = np.array([[0, 3, 7, 9, 14, 20], [2, 2, 5, 8, 11, 13]])
+    kv = [15, 10]
+    ours = O.dense_attention(Q, K, V, qp, kv, scale=0.3)
+    ref = _sdpa_ref(Q, K, V, qp, kv, 0.3)
+    assert np.allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_values_alias_latent_rows():
+    rng = np.random.default_rng(12)
+    lat = rng.standard_normal((1, 30, 1, 40))
+    Q = rng.standard_normal((1, 3, 4, 40))
+    qp = np.array([[5, 17, 29]])
+    ours = O.dense_attention(Q, lat, lat[..., :32], qp)
+    ref = _sdpa_ref(Q, lat, np.ascontiguousarray(lat[..., :32]), qp, [30], 1 / math.sqrt(40))
+    assert np.allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_equals_dense_exactly_when_topk_covers_everything():
+    rng = np.random.default_rng(13)
+    S, n_q, n_kv = 1, 20, 20
+    Q = rng.standard_normal((S, n_q, 4, 16))
+    K = rng.standard_normal((S, n_kv, 2, 16))
+    V = rng.standard_normal((S, n_kv, 2, 16))
+    q_idx = rng.standard_normal((S, n_q, 3, 32))
+    k_idx = rng.standard_normal((S, n_kv, 32))
+    w = rng.standard_normal((S, n_q, 3))
+    qp = np.arange(n_q)[None, :]
+    o_sparse, idx, _ = O.forward(Q, K, V, q_idx, k_idx, w, 32, 1, qp)
+    o_dense = O.dense_attention(Q, K, V, qp)
+    assert np.array_equal(o_sparse, o_dense)
+    # block mode below the threshold (top_k + c - 1 = 23 >= 20 tokens) is dense too
+    o_blk, _, _ = O.forward(Q, K, V, q_idx, k_idx, w, 20, 4, qp)
+    assert np.array_equal(o_blk, o_dense)
+
+
+def test_single_selected_key_returns_its_value():
+    rng = np.random.default_rng(14)
+    Q = rng.standard_normal((1, 1, 4, 8))
+    K = rng.standard_normal((1, 10, 1, 8))
+    V = rng.standard_normal((1, 10, 1, 8))
+    o = O.sparse_attention(Q, K, V, np.array([[[6]]]), np.array([[9]]))
+    assert np.array_equal(o[0, 0], np.repeat(V[0, 6], 4, axis=0))
+    # empty and invisible selections give zero rows, never NaN
+    o = O.sparse_attention(Q, K, V, np.array([[[-1]]]), np.array([[9]]))
+    assert np.array_equal(o, np.zeros_like(o))
+    o = O.sparse_attention(Q, K, V, np.array([[[3]]]), np.array([[-1]]))
+    assert np.array_equal(o, np.zeros_like(o))
+
+
+def test_attention_token_order_only_changes_rounding():
+    rng = np.random.default_rng(15)
+    Q = rng.standard_normal((1, 1, 4, 8))
+    K = rng.standard_normal((1, 40, 2, 8))
+    V = rng.standard_normal((1, 40, 2, 8))
+    a = O.sparse_attention(Q, K, V, np.array([[[3, 9, 17, 30, 31]]]), np.array([[39]]))
+    b = O.sparse_attention(Q, K, V, np.array([[[31, 17, 3, 30, 9]]]), np.array([[39]]))
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
