@@ -1,0 +1,380 @@
+// Lightning-indexer scores on gfx950.
+//
+//   s(i, u) = sum_h w(i, h) * max(0, q'(i, h) . k(u)) [* k_scale(u)]
+//
+// (ik_llama.cpp PR #2058, first commit: per-head ReLU of the key/query
+// product, weighted head sum, causal mask; llama.cpp mirror commit c88c916636,
+// last paragraph: the ReLU acts on each head before the sum.)  The per-head
+// products are never written out: they live in MFMA accumulators and the ReLU,
+// the head weights and the head sum run in the epilogue (ik_llama_opt log,
+// fused indexer top-k commit).
+//
+// MFMA kernel layout (D = 128, H <= 64):
+//   one wave = one query row x one chunk of 32-unit tiles.  Rows of the MFMA
+//   are heads (32 per row block, up to 2 blocks), columns are 32 keys, the
+//   contraction runs over the 128 dims in 8 steps of 16.  The contraction
+//   order is permuted so that lane half h reads dims [64h, 64h + 64) of its
+//   key: each lane streams 64 contiguous dims, and the same permutation is
+//   applied to q.  The head sum is an in-lane sum of 16 accumulators per row
+//   block plus one exchange between lane halves.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+enum KeyKind { KK_BF16 = 0, KK_F16 = 1, KK_FP8 = 2, KK_F32 = 3 };
+
+template <int KK>
+struct KeyTile;  // raw bytes of one lane's 64 dims of one key
+
+template <> struct KeyTile<KK_BF16> { u32x4_t v[8]; };
+template <> struct KeyTile<KK_F16> { u32x4_t v[8]; };
+template <> struct KeyTile<KK_FP8> { u32x4_t v[4]; };
+template <> struct KeyTile<KK_F32> { u32x4_t v[16]; };
+
+template <int KK>
+__device__ __forceinline__ void load_key(KeyTile<KK>& t, const void* base, int64_t elem_off, bool ok) {
+  constexpr int N = sizeof(KeyTile<KK>) / 16;
+  constexpr int ESZ = KK == KK_FP8 ? 1 : (KK == KK_F32 ? 4 : 2);
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(
+      static_cast<const char*>(base) + elem_off * ESZ);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (ok) t.v[i] = p[i];
+    else t.v[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// B operand(s) of contraction step ks from a lane's key slice.
+template <int KK>
+__device__ __forceinline__ void key_operand(const KeyTile<KK>& t, int ks, u32x4_t& hi, u32x4_t& lo) {
+  if constexpr (KK == KK_BF16 || KK == KK_F16) {
+    hi = t.v[ks];
+  } else if constexpr (KK == KK_FP8) {
+    const u32x4_t v = t.v[ks >> 1];
+    const uint32_t a = (ks & 1) ? v.z : v.x;
+    const uint32_t b = (ks & 1) ? v.w : v.y;
+    u32x2_t ca = fp8x4_to_f16x4_scaled(a), cb = fp8x4_to_f16x4_scaled(b);
+    hi = u32x4_t{ca.x, ca.y, cb.x, cb.y};
+  } else {
+    const u32x4_t a = t.v[2 * ks], b = t.v[2 * ks + 1];
+    float f[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
+                  __uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float h0 = bf16_to_f32(f32_to_bf16(f[2 * i])), h1 = bf16_to_f32(f32_to_bf16(f[2 * i + 1]));
+      h[i] = pack_bf16x2(h0, h1);
+      l[i] = pack_bf16x2(f[2 * i] - h0, f[2 * i + 1] - h1);
+    }
+    hi = u32x4_t{h[0], h[1], h[2], h[3]};
+    lo = u32x4_t{l[0], l[1], l[2], l[3]};
+  }
+}
+
+// Unnormalised Walsh-Hadamard butterflies on the 6 in-lane index bits of x[64].
+__device__ __forceinline__ void fwht64(float (&x)[64]) {
+#pragma unroll
+  for (int b = 1; b < 64; b <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (i & b) continue;
+      const float u = x[i], v = x[i | b];
+      x[i] = u + v;
+      x[i | b] = u - v;
+    }
+  }
+}
+
+template <int KK, int QK, int RB, int NQ>
+__global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
+  constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
+  constexpr int NK = KK == KK_F32 ? 2 : 1;
+  extern __shared__ uint32_t s_hist[];
+
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, h2 = lane >> 5;
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  int64_t row;
+  int chunk;
+  if (p.chunk_major) {
+    const int ncg = (p.n_chunks + 3) >> 2;
+    row = blockIdx.x / ncg;
+    chunk = (blockIdx.x % ncg) * 4 + wid;
+  } else {
+    const int64_t nrg = (rows + 3) >> 2;
+    row = (nrg - 1 - static_cast<int64_t>(blockIdx.x) / p.n_chunks) * 4 + wid;
+    chunk = blockIdx.x % p.n_chunks;
+  }
+  const bool use_hist = p.hist != nullptr;
+  if (use_hist) {
+    for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = 0;
+    __syncthreads();
+  }
+
+  bool active = row < rows && chunk < p.n_chunks;
+  const int s = active ? static_cast<int>(row / p.n_q) : 0;
+  int64_t n_vis = 0, u_begin = 0, u_end = 0;
+  if (active) {
+    const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
+    n_vis = visible_tokens(p.q_pos[row], kl, p.n_units * p.c) / p.c;
+    u_begin = static_cast<int64_t>(chunk) * p.chunk_tiles * 32;
+    u_end = u_begin + static_cast<int64_t>(p.chunk_tiles) * 32;
+    if (u_end > p.n_units) u_end = p.n_units;
+  }
+  const int64_t c_end = n_vis < u_end ? n_vis : u_end;     // compute [u_begin, c_end)
+  const bool do_hist = use_hist && n_vis > p.k_out;
+  const int64_t nf = (p.c == 1 && p.n_sink < n_vis) ? p.n_sink : (p.c == 1 ? n_vis : 0);
+
+  if (active && c_end > u_begin) {
+    // ---------------------------------------------------- query operand --
+    const int Hh = p.H;
+    u32x4_t qa[RB][8][NQ];
+    float fw[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int head = rb * 32 + n;
+      float x[64];
+      if (head < Hh) {
+        const int64_t base = (row * Hh + head) * 128 + 64 * h2;
+        if constexpr (QK == 0 || QK == 1) {
+          const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.q) + base);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const u32x4_t v = qp[i];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint16_t lo16 = w4[j] & 0xffffu, hi16 = w4[j] >> 16;
+              x[8 * i + 2 * j] = QK == 0 ? bf16_to_f32(lo16) : f16_to_f32(lo16);
+              x[8 * i + 2 * j + 1] = QK == 0 ? bf16_to_f32(hi16) : f16_to_f32(hi16);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) x[i] = 0.f;
+      }
+      if (p.hadamard) {
+        fwht64(x);
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+          const float o = __shfl_xor(x[i], 32, 64);
+          x[i] = (h2 == 0 ? x[i] + o : o - x[i]) * 0.088388347648318440550f;   // 1/sqrt(128)
+        }
+      }
+      float factor = 1.f;
+      if constexpr (F16OP) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        int e = 0;
+        if (amax > 0.f) {
+          int E;
+          frexpf(amax, &E);
+          e = 14 - E;   // amax * 2^e < 2^14: inside the f16 range with headroom
+        }
+        factor = ldexpf(1.f, -e);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          uint32_t wv4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            wv4[j] = pack_f16x2(ldexpf(x[8 * ks + 2 * j], e), ldexpf(x[8 * ks + 2 * j + 1], e));
+          qa[rb][ks][0] = u32x4_t{wv4[0], wv4[1], wv4[2], wv4[3]};
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          uint32_t hv[4], lv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = x[8 * ks + 2 * j], b = x[8 * ks + 2 * j + 1];
+            const float ah = bf16_to_f32(f32_to_bf16(a)), bh = bf16_to_f32(f32_to_bf16(b));
+            hv[j] = pack_bf16x2(ah, bh);
+            lv[j] = pack_bf16x2(a - ah, b - bh);
+          }
+          qa[rb][ks][0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+          if constexpr (NQ == 2) qa[rb][ks][NQ - 1] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+        }
+      }
+      float wh = head < Hh ? p.w[row * Hh + head] : 0.f;
+      if constexpr (KK == KK_FP8) factor *= 256.f;   // undo the 2^-8 of the fp8 -> f16 map
+      fw[rb] = wh * factor;
+    }
+
+    // head weight of each accumulator row held by this lane
+    float wv[RB][16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) wv[rb][j] = __shfl(fw[rb], 8 * (j >> 2) + 4 * h2 + (j & 3), 64);
+
+    // -------------------------------------------------------- key stream --
+    const int64_t key_row0 = static_cast<int64_t>(s) * p.n_units;
+    const int t_begin = static_cast<int>(u_begin >> 5);
+    const int t_end = static_cast<int>((c_end + 31) >> 5);
+    KeyTile<KK> cur, nxt;
+    {
+      const int64_t u = static_cast<int64_t>(t_begin) * 32 + n;
+      load_key<KK>(cur, p.k, (key_row0 + (u < p.n_units ? u : 0)) * 128 + 64 * h2, u < p.n_units);
+    }
+    for (int t = t_begin; t < t_end; ++t) {
+      if (t + 1 < t_end) {
+        const int64_t u = static_cast<int64_t>(t + 1) * 32 + n;
+        load_key<KK>(nxt, p.k, (key_row0 + (u < p.n_units ? u : 0)) * 128 + 64 * h2, u < p.n_units);
+      }
+      f32x16_t acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4_t bh, bl;
+        key_operand<KK>(cur, ks, bh, bl);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (F16OP) {
+            acc[rb] = mfma32x32x16_f16(qa[rb][ks][0], bh, acc[rb]);
+          } else {
+            acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bh, acc[rb]);
+            if constexpr (NK == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bl, acc[rb]);
+            if constexpr (NQ == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][NQ - 1], bh, acc[rb]);
+          }
+        }
+      }
+      // epilogue: ReLU, head weight, head sum
+      float part = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part = fmaf(wv[rb][j], fmaxf(acc[rb][j], 0.f), part);
+      float tot = part + __shfl_xor(part, 32, 64);
+      const int64_t u = static_cast<int64_t>(t) * 32 + n;
+      if constexpr (KK == KK_FP8) {
+        if (u < p.n_units) tot *= p.k_scale[key_row0 + u];
+      }
+      const float val = u < n_vis ? tot : NEG_INF;
+      if (h2 == 0 && u < u_end) p.scores[row * p.n_units + u] = val;
+      if (do_hist && h2 == 0 && u >= nf && u < n_vis) atomicAdd(&s_hist[order_key(val) >> 20], 1u);
+      cur = nxt;
+    }
+  }
+  if (active && p.fill_invisible) {
+    const int64_t f0 = c_end > u_begin ? ((c_end + 31) & ~int64_t(31)) : u_begin;
+    for (int64_t u = f0 + lane; u < u_end; u += 64) p.scores[row * p.n_units + u] = NEG_INF;
+    // the partially computed last tile already holds -inf past n_vis
+  }
+  if (use_hist) {
+    __syncthreads();
+    if (row < rows) {
+      uint32_t* g = p.hist + row * HIST_BINS;
+      for (int b = threadIdx.x; b < HIST_BINS; b += 256) {
+        const uint32_t v = s_hist[b];
+        if (v) atomicAdd(g + b, v);
+      }
+    }
+  }
+}
+
+// Generic path: any element types, H <= 128, D <= 256.  One thread per
+// (row, unit); the row's (rotated) query and weights sit in LDS.
+__global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
+  extern __shared__ float s_q[];   // [H * D] then w[H]
+  const int64_t n_ub = (p.n_units + 255) / 256;
+  const int64_t row = blockIdx.x / n_ub;
+  const int64_t ublk = blockIdx.x % n_ub;
+  const int s = static_cast<int>(row / p.n_q);
+  const int H = p.H, D = p.D;
+  float* s_w = s_q + H * D;
+  for (int i = threadIdx.x; i < H * D; i += 256) s_q[i] = load_elem(p.q, row * H * D + i, p.q_dtype);
+  for (int i = threadIdx.x; i < H; i += 256) s_w[i] = p.w[row * H + i];
+  __syncthreads();
+  if (p.hadamard) {   // D == 128: butterflies over the 7 index bits, then 1/sqrt(128)
+    for (int b = 1; b < D; b <<= 1) {
+      for (int i = threadIdx.x; i < H * D / 2; i += 256) {
+        const int h = i / (D / 2), r = i % (D / 2);
+        const int lo = (r / b) * 2 * b + (r % b), hi = lo + b;
+        const float u = s_q[h * D + lo], v = s_q[h * D + hi];
+        s_q[h * D + lo] = u + v;
+        s_q[h * D + hi] = u - v;
+      }
+      __syncthreads();
+    }
+    for (int i = threadIdx.x; i < H * D; i += 256) s_q[i] *= 0.088388347648318440550f;
+    __syncthreads();
+  }
+  const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
+  const int64_t n_vis = visible_tokens(p.q_pos[row], kl, p.n_units * p.c) / p.c;
+  const int64_t u = ublk * 256 + threadIdx.x;
+  if (u >= p.n_units) return;
+  float val = NEG_INF;
+  if (u < n_vis) {
+    const int64_t kb = (static_cast<int64_t>(s) * p.n_units + u) * D;
+    float tot = 0.f;
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(s_q[h * D + d], load_elem(p.k, kb + d, p.k_dtype), dot);
+      tot = fmaf(s_w[h], fmaxf(dot, 0.f), tot);
+    }
+    if (p.k_dtype == DSA_FP8_E4M3) tot *= p.k_scale[static_cast<int64_t>(s) * p.n_units + u];
+    val = tot;
+  }
+  p.scores[row * p.n_units + u] = val;
+}
+
+bool scores_use_mfma(int q_dtype, int k_dtype, int H, int D) {
+  return D == 128 && H <= 64 && (q_dtype == DSA_BF16 || q_dtype == DSA_F16);
+}
+
+template <int KK, int QK, int NQ>
+static hipError_t launch_mfma_rb(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  if (p.H <= 32)
+    hipLaunchKernelGGL((score_mfma_kernel<KK, QK, 1, NQ>), grid, dim3(256), lds, st, p);
+  else
+    hipLaunchKernelGGL((score_mfma_kernel<KK, QK, 2, NQ>), grid, dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
+// q enters the MFMA as one f16 operand (f16/fp8 keys, after a power-of-two
+// prescale) or as bf16; a bf16 q that is not rotated is exact in one bf16
+// operand, anything else is split into a bf16 high part and a bf16 residual.
+template <int KK>
+static hipError_t launch_mfma_q(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
+  const bool split = !F16OP && (p.q_dtype != DSA_BF16 || p.hadamard);
+  if (p.q_dtype == DSA_BF16)
+    return split ? launch_mfma_rb<KK, 0, 2>(p, grid, lds, st) : launch_mfma_rb<KK, 0, 1>(p, grid, lds, st);
+  return split ? launch_mfma_rb<KK, 1, 2>(p, grid, lds, st) : launch_mfma_rb<KK, 1, 1>(p, grid, lds, st);
+}
+
+hipError_t launch_scores(ScoreParams p, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  if (!scores_use_mfma(p.q_dtype, p.k_dtype, p.H, p.D)) {
+    const size_t lds = (static_cast<size_t>(p.H) * p.D + p.H) * sizeof(float);
+    dim3 grid(static_cast<unsigned>(((p.n_units + 255) / 256) * rows));
+    hipLaunchKernelGGL(score_valu_kernel, grid, dim3(256), lds, st, p);
+    return hipGetLastError();
+  }
+  const int64_t n_tiles = (p.n_units + 31) / 32;
+  // Long rows: chunks of up to 32 tiles per wave; short rows spread over 4 waves.
+  int64_t ct = (n_tiles + 3) / 4;
+  if (ct > 32) ct = 32;
+  if (ct < 1) ct = 1;
+  p.chunk_tiles = static_cast<int32_t>(ct);
+  p.n_chunks = static_cast<int32_t>((n_tiles + ct - 1) / ct);
+  p.chunk_major = p.hist != nullptr ? 1 : 0;
+  dim3 grid;
+  if (p.chunk_major) grid = dim3(static_cast<unsigned>(rows * ((p.n_chunks + 3) / 4)));
+  else grid = dim3(static_cast<unsigned>(((rows + 3) / 4) * p.n_chunks));
+  const size_t lds = p.hist ? HIST_BINS * sizeof(uint32_t) : 0;
+  switch (p.k_dtype) {
+    case DSA_BF16: return launch_mfma_q<KK_BF16>(p, grid, lds, st);
+    case DSA_F16: return launch_mfma_q<KK_F16>(p, grid, lds, st);
+    case DSA_FP8_E4M3: return launch_mfma_q<KK_FP8>(p, grid, lds, st);
+    default: return launch_mfma_q<KK_F32>(p, grid, lds, st);
+  }
+}
+
+}  // namespace dsa

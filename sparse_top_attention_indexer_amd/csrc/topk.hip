@@ -1,0 +1,433 @@
+// Per-row top-k selection on gfx950, without a full sort.
+//
+// Selection rule (ik_llama.cpp PR #2058, first commit: top-k of
+// min(top_k, n_tokens) after the causal mask; "UPDATE 5" commit: the sink keys
+// of the query's own sequence are forced in; llama.cpp mirror commit
+// c88c916636: in block mode the budget is top_k / compress_ratio blocks):
+//   K = min(k_out, n_vis); forced = units 0 .. min(n_sink, n_vis) - 1;
+//   the other K - |forced| units are the best of the remaining visible units
+//   by (score descending, index ascending); output ascending, -1 padded.
+//
+// Scores become order-preserving 32-bit keys.  A radix select over the keys
+// finds the threshold key T and how many units equal to T are kept (the
+// lowest-indexed ones); an ordered compaction then writes the kept indices in
+// ascending order.
+//   - short rows (<= 16384 units, or many rows): one workgroup per row, the
+//     row's keys live in LDS, three histogram passes of 12 + 12 + 8 bits;
+//   - long rows with few of them (decode): many workgroups per row.  A global
+//     histogram of the top 12 bits (built by the score epilogue in the fused
+//     path) locates the threshold bin; units of that bin are gathered as
+//     candidates; one workgroup per row resolves the exact threshold among
+//     the candidates; the row is then compacted chunk by chunk.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+struct RowInfo {
+  int64_t n_vis;   // visible units
+  int64_t nf;      // forced sinks
+  int64_t K;       // kept units
+};
+
+__device__ __forceinline__ RowInfo row_info(const TopkParams& p, int64_t row) {
+  const int s = static_cast<int>(row / p.n_q);
+  const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
+  RowInfo r;
+  r.n_vis = visible_tokens(p.q_pos[row], kl, p.n_units * p.c) / p.c;
+  r.nf = p.c == 1 ? (p.n_sink < r.n_vis ? p.n_sink : r.n_vis) : 0;
+  r.K = p.k_out < r.n_vis ? p.k_out : r.n_vis;
+  return r;
+}
+
+// Finds the bin b (scanning from the highest bin down) that holds the need-th
+// largest element: above(b) < need <= above(b) + hist[b], with above(b) the
+// count of elements in bins > b.  256 threads; nb a multiple of 256.
+// Returns b and sets *above.  All threads get the result.
+__device__ uint32_t find_bin_desc(const uint32_t* hist, int nb, uint32_t need, uint32_t* scratch,
+                                  uint32_t* above) {
+  const int per = nb / 256;
+  // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 owns the top bins
+  const int hi = nb - threadIdx.x * per;
+  uint32_t local = 0;
+  for (int b = hi - per; b < hi; ++b) local += hist[b];
+  uint32_t total;
+  const uint32_t excl = block_excl_scan_256(local, scratch, &total);  // elements in higher bins
+  if (excl < need && need <= excl + local) {
+    uint32_t acc = excl;
+    for (int b = hi - 1; b >= hi - per; --b) {
+      if (acc + hist[b] >= need) {
+        scratch[4] = static_cast<uint32_t>(b);
+        scratch[5] = acc;
+        break;
+      }
+      acc += hist[b];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = scratch[4];
+  *above = scratch[5];
+  __syncthreads();
+  return bin;
+}
+
+// ------------------------------------------------------- one-row-per-block --
+
+__global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
+  extern __shared__ uint32_t s_mem[];
+  uint32_t* s_hist = s_mem;                 // HIST_BINS
+  uint32_t* s_scr = s_mem + HIST_BINS;      // 16
+  uint32_t* s_key = s_scr + 16;             // row keys
+  const int64_t row = blockIdx.x;
+  const RowInfo ri = row_info(p, row);
+  int32_t* out = p.idx + row * p.k_out;
+  const int tid = threadIdx.x;
+
+  if (ri.n_vis <= p.k_out) {   // everything visible is kept
+    for (int64_t j = tid; j < p.k_out; j += 256) out[j] = j < ri.n_vis ? static_cast<int32_t>(j) : -1;
+    return;
+  }
+  const int64_t m = ri.n_vis - ri.nf;             // candidates: units nf .. n_vis-1
+  const uint32_t need0 = static_cast<uint32_t>(ri.K - ri.nf);
+  const float* sc = p.scores + row * p.n_units + ri.nf;
+  for (int64_t e = tid; e < m; e += 256) s_key[e] = order_key(sc[e]);
+  for (int64_t j = tid; j < p.k_out; j += 256) {
+    if (j < ri.nf) out[j] = static_cast<int32_t>(j);
+    else if (j >= ri.K) out[j] = -1;
+  }
+  if (need0 == 0) return;   // every kept slot is a forced sink
+  __syncthreads();
+
+  // radix select: 12 + 12 + 8 bits
+  uint32_t prefix = 0, pmask = 0, need = need0;
+  const int shifts[3] = {20, 8, 0};
+  const int nbits[3] = {12, 12, 8};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int nb = 1 << nbits[pass], sh = shifts[pass];
+    for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
+    __syncthreads();
+    for (int64_t e = tid; e < m; e += 256) {
+      const uint32_t k = s_key[e];
+      if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t above;
+    const uint32_t b = find_bin_desc(s_hist, nb, need, s_scr, &above);
+    need -= above;
+    prefix |= b << sh;
+    pmask |= static_cast<uint32_t>(nb - 1) << sh;
+  }
+  const uint32_t T = prefix;      // threshold key; keep `need` units equal to T (lowest index)
+
+  // ordered compaction: thread t owns a contiguous range of candidates
+  const int64_t per = (m + 255) / 256;
+  const int64_t e0 = tid * per < m ? tid * per : m;
+  const int64_t e1 = e0 + per < m ? e0 + per : m;
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int64_t e = e0; e < e1; ++e) {
+    const uint32_t k = s_key[e];
+    n_gt += k > T;
+    n_eq += k == T;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block_excl_scan_256(n_eq, s_scr, &tot);
+  uint32_t take_eq = need > eq_before ? need - eq_before : 0;
+  if (take_eq > n_eq) take_eq = n_eq;
+  const uint32_t pos0 = block_excl_scan_256(n_gt + take_eq, s_scr, &tot);
+  uint32_t pos = static_cast<uint32_t>(ri.nf) + pos0, eq_seen = 0;
+  for (int64_t e = e0; e < e1; ++e) {
+    const uint32_t k = s_key[e];
+    bool keep = k > T;
+    if (k == T) {
+      keep = eq_seen < take_eq;
+      ++eq_seen;
+    }
+    if (keep) {
+      if (pos < ri.K) out[pos] = static_cast<int32_t>(ri.nf + e);   // guard: never past K
+      ++pos;
+    }
+  }
+}
+
+// --------------------------------------------------------- multi-block path --
+
+__global__ void topk_clear_kernel(TopkParams p) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const int64_t n = rows * HIST_BINS;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    p.hist[i] = 0;
+    if (i < rows) p.cand_cnt[i] = 0;
+  }
+}
+
+// Top-12-bit histogram of the candidate units of each row (standalone top-k;
+// the fused path gets it from the score epilogue instead).
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
+  __shared__ uint32_t s_hist[HIST_BINS];
+  const int64_t row = blockIdx.x / p.n_chunks;
+  const int ch = blockIdx.x % p.n_chunks;
+  const RowInfo ri = row_info(p, row);
+  if (ri.n_vis <= p.k_out) return;
+  for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = 0;
+  __syncthreads();
+  int64_t j0 = static_cast<int64_t>(ch) * p.chunk, j1 = j0 + p.chunk;
+  if (j0 < ri.nf) j0 = ri.nf;
+  if (j1 > ri.n_vis) j1 = ri.n_vis;
+  const float* sc = p.scores + row * p.n_units;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) atomicAdd(&s_hist[order_key(sc[j]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* g = p.hist + row * HIST_BINS;
+  for (int b = threadIdx.x; b < HIST_BINS; b += 256)
+    if (s_hist[b]) atomicAdd(g + b, s_hist[b]);
+}
+
+// Threshold bin per row; counts units above it per chunk; gathers the units
+// of the threshold bin as candidates.
+__global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
+  __shared__ uint32_t s_hist[HIST_BINS];
+  __shared__ uint32_t s_scr[16];
+  __shared__ uint32_t s_cnt, s_base;
+  const int64_t row = blockIdx.x / p.n_chunks;
+  const int ch = blockIdx.x % p.n_chunks;
+  const RowInfo ri = row_info(p, row);
+  if (ri.n_vis <= p.k_out) return;
+  const uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
+  if (need == 0) return;
+  const uint32_t* g = p.hist + row * HIST_BINS;
+  for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = g[b];
+  if (threadIdx.x == 0) s_cnt = 0;
+  __syncthreads();
+  uint32_t above;
+  const uint32_t b1 = find_bin_desc(s_hist, HIST_BINS, need, s_scr, &above);
+  if (ch == 0 && threadIdx.x == 0) {
+    p.thr[row * 4 + 0] = b1;
+    p.thr[row * 4 + 3] = above;
+  }
+  int64_t j0 = static_cast<int64_t>(ch) * p.chunk, j1 = j0 + p.chunk;
+  if (j0 < ri.nf) j0 = ri.nf;
+  if (j1 > ri.n_vis) j1 = ri.n_vis;
+  const float* sc = p.scores + row * p.n_units;
+  // pass 1: count units above the bin and units in it
+  uint32_t n_hi = 0, n_in = 0;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
+    const uint32_t bin = order_key(sc[j]) >> 20;
+    n_hi += bin > b1;
+    n_in += bin == b1;
+  }
+  uint32_t tot_hi, tot_in;
+  block_excl_scan_256(n_hi, s_scr, &tot_hi);
+  const uint32_t my_off = block_excl_scan_256(n_in, s_scr, &tot_in);
+  if (threadIdx.x == 0) {
+    p.cnt_hi[row * p.n_chunks + ch] = tot_hi;
+    s_base = tot_in ? atomicAdd(p.cand_cnt + row, tot_in) : 0;
+  }
+  __syncthreads();
+  // pass 2: write the candidates (key, index)
+  uint32_t w = s_base + my_off;
+  uint32_t* cand = p.cand + row * p.cand_cap * 2;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
+    const uint32_t k = order_key(sc[j]);
+    if ((k >> 20) == b1) {
+      if (w < p.cand_cap) {
+        cand[2 * w] = k;
+        cand[2 * w + 1] = static_cast<uint32_t>(j);
+      }
+      ++w;
+    }
+  }
+}
+
+// Exact threshold among the candidates of one row, per-chunk output offsets,
+// the forced sinks and the -1 padding.
+__global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
+  __shared__ uint32_t s_hist[HIST_BINS];
+  __shared__ uint32_t s_scr[16];
+  extern __shared__ uint32_t s_chunk[];   // n_chunks selected-candidate counters
+  const int64_t row = blockIdx.x;
+  const RowInfo ri = row_info(p, row);
+  int32_t* out = p.idx + row * p.k_out;
+  const int tid = threadIdx.x;
+  if (ri.n_vis <= p.k_out) {
+    for (int64_t j = tid; j < p.k_out; j += 256) out[j] = j < ri.n_vis ? static_cast<int32_t>(j) : -1;
+    return;
+  }
+  for (int64_t j = tid; j < p.k_out; j += 256) {
+    if (j < ri.nf) out[j] = static_cast<int32_t>(j);
+    else if (j >= ri.K) out[j] = -1;
+  }
+  uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
+  uint32_t T = 0xffffffffu, J = 0;
+  bool none = need == 0;
+  const uint32_t* cand = p.cand + row * p.cand_cap * 2;
+  const uint32_t m = none ? 0 : p.cand_cnt[row];
+  if (!none) {
+    need -= p.thr[row * 4 + 3];            // minus the units above the threshold bin
+    const uint32_t b1 = p.thr[row * 4 + 0];
+    // low 20 bits of the key: 12 + 8
+    uint32_t prefix = b1 << 20, pmask = 0xfff00000u;
+    const int shifts[2] = {8, 0};
+    const int nbits[2] = {12, 8};
+    for (int pass = 0; pass < 2; ++pass) {
+      const int nb = 1 << nbits[pass], sh = shifts[pass];
+      for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
+      __syncthreads();
+      for (uint32_t e = tid; e < m; e += 256) {
+        const uint32_t k = cand[2 * e];
+        if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t above;
+      const uint32_t b = find_bin_desc(s_hist, nb, need, s_scr, &above);
+      need -= above;
+      prefix |= b << sh;
+      pmask |= static_cast<uint32_t>(nb - 1) << sh;
+    }
+    T = prefix;
+    // the need-th smallest index among candidates equal to T: radix select on
+    // the complemented index (largest complement = smallest index), 3 x 11 bits
+    uint32_t jp = 0, jm = 0;
+    const int jsh[3] = {21, 10, 0};
+    const int jbits[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int nb = 1 << jbits[pass], sh = jsh[pass];
+      for (int b = tid; b < HIST_BINS; b += 256) s_hist[b] = 0;
+      __syncthreads();
+      for (uint32_t e = tid; e < m; e += 256) {
+        if (cand[2 * e] != T) continue;
+        const uint32_t cj = ~cand[2 * e + 1];
+        if ((cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t above;
+      const uint32_t b = find_bin_desc(s_hist, nb < 256 ? 256 : nb, need, s_scr, &above);
+      need -= above;
+      jp |= b << sh;
+      jm |= static_cast<uint32_t>(nb - 1) << sh;
+    }
+    J = ~jp;
+  }
+  // per-chunk counts of selected candidates, then output offsets
+  for (int c = tid; c < p.n_chunks; c += 256) s_chunk[c] = 0;
+  __syncthreads();
+  for (uint32_t e = tid; e < m; e += 256) {
+    const uint32_t k = cand[2 * e], j = cand[2 * e + 1];
+    if (k > T || (k == T && j <= J)) atomicAdd(&s_chunk[j / p.chunk], 1u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = static_cast<uint32_t>(ri.nf);
+    for (int c = 0; c < p.n_chunks; ++c) {
+      p.offs[row * p.n_chunks + c] = acc;
+      acc += p.cnt_hi[row * p.n_chunks + c] + s_chunk[c];
+    }
+    p.thr[row * 4 + 1] = T;
+    p.thr[row * 4 + 2] = J;
+  }
+}
+
+// Ordered compaction of one chunk of a row.
+__global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
+  __shared__ uint32_t s_scr[16];
+  const int64_t row = blockIdx.x / p.n_chunks;
+  const int ch = blockIdx.x % p.n_chunks;
+  const RowInfo ri = row_info(p, row);
+  if (ri.n_vis <= p.k_out || ri.K == ri.nf) return;
+  const uint32_t T = p.thr[row * 4 + 1], J = p.thr[row * 4 + 2];
+  int64_t j0 = static_cast<int64_t>(ch) * p.chunk, j1 = j0 + p.chunk;
+  if (j0 < ri.nf) j0 = ri.nf;
+  if (j1 > ri.n_vis) j1 = ri.n_vis;
+  const int64_t len = j1 > j0 ? j1 - j0 : 0;
+  const int64_t per = (len + 255) / 256;
+  const int64_t a0 = j0 + (threadIdx.x * per < len ? threadIdx.x * per : len);
+  const int64_t a1 = a0 + per < j1 ? a0 + per : j1;
+  const float* sc = p.scores + row * p.n_units;
+  uint32_t cnt = 0;
+  for (int64_t j = a0; j < a1; ++j) {
+    const uint32_t k = order_key(sc[j]);
+    cnt += (k > T || (k == T && static_cast<uint32_t>(j) <= J));
+  }
+  uint32_t tot;
+  uint32_t pos = p.offs[row * p.n_chunks + ch] + block_excl_scan_256(cnt, s_scr, &tot);
+  int32_t* out = p.idx + row * p.k_out;
+  for (int64_t j = a0; j < a1; ++j) {
+    const uint32_t k = order_key(sc[j]);
+    if (k > T || (k == T && static_cast<uint32_t>(j) <= J)) {
+      if (pos < ri.K) out[pos] = static_cast<int32_t>(j);   // guard: never past K
+      ++pos;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host --
+
+bool topk_use_multiblock(int64_t rows, int64_t n_units) {
+  return n_units > 16384 || (rows < 128 && n_units > TOPK_CHUNK);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t topk_workspace_bytes(int64_t rows, int64_t n_units) {
+  if (!topk_use_multiblock(rows, n_units)) return 0;
+  const int64_t nch = (n_units + TOPK_CHUNK - 1) / TOPK_CHUNK;
+  size_t b = 0;
+  b += align256(rows * HIST_BINS * 4);
+  b += align256(rows * 4);
+  b += align256(rows * n_units * 8);
+  b += align256(rows * nch * 4) * 2;
+  b += align256(rows * 16);
+  return b;
+}
+
+void topk_bind_workspace(TopkParams& p, void* ws) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  p.chunk = TOPK_CHUNK;
+  p.n_chunks = static_cast<int32_t>((p.n_units + TOPK_CHUNK - 1) / TOPK_CHUNK);
+  p.cand_cap = p.n_units;
+  char* c = static_cast<char*>(ws);
+  p.hist = reinterpret_cast<uint32_t*>(c);     c += align256(rows * HIST_BINS * 4);
+  p.cand_cnt = reinterpret_cast<uint32_t*>(c); c += align256(rows * 4);
+  p.cand = reinterpret_cast<uint32_t*>(c);     c += align256(rows * p.n_units * 8);
+  p.cnt_hi = reinterpret_cast<uint32_t*>(c);   c += align256(rows * p.n_chunks * 4);
+  p.offs = reinterpret_cast<uint32_t*>(c);     c += align256(rows * p.n_chunks * 4);
+  p.thr = reinterpret_cast<uint32_t*>(c);
+}
+
+hipError_t launch_topk_clear(const TopkParams& p, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  int64_t blocks = (rows * HIST_BINS + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(topk_clear_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  if (!topk_use_multiblock(rows, p.n_units)) {
+    const size_t lds = (HIST_BINS + 16 + static_cast<size_t>(p.n_units)) * sizeof(uint32_t);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_row_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
+    return hipGetLastError();
+  }
+  const dim3 g(static_cast<unsigned>(rows * p.n_chunks));
+  hipError_t e;
+  if (!hist_ready) {
+    if ((e = launch_topk_clear(p, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_hist_kernel, g, dim3(256), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_select_kernel, g, dim3(256), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<unsigned>(rows)), dim3(256),
+                     p.n_chunks * sizeof(uint32_t), st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_compact_kernel, g, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

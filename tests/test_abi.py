@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/dsa.h declares, descriptor layouts agree with the binding, and every
+argument check fails before anything is launched.
+
+The error-path calls pass fake (never dereferenced) device addresses, so they
+run only where no GPU is visible."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_top_attention_indexer_amd as dsa
+from sparse_top_attention_indexer_amd import AttnDesc, ForwardDesc, IndexDesc, TopkDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="error-path calls use fake device addresses")
+
+OK, NULL, SHAPE, DTYPE, PARAM, ALIGN, WORKSPACE, HIP, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+FAKE = 0x10000   # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_functions_are_exported_and_bound():
+    L = dsa.lib()
+    names = declared_functions()
+    assert "dsa_forward" in names and "dsa_topk" in names and len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in dsa.SYMBOLS, n
+
+
+def test_descriptor_layouts_match():
+    L = dsa.lib()
+    for which, cls in enumerate((IndexDesc, TopkDesc, AttnDesc, ForwardDesc)):
+        assert L.dsa_desc_size(which) == ctypes.sizeof(cls)
+    assert L.dsa_desc_size(7) == 0
+    assert L.dsa_version() >= 100
+    for code in (OK, NULL, SHAPE, DTYPE, PARAM, ALIGN, WORKSPACE, HIP, UNSUP, 42):
+        assert isinstance(L.dsa_strerror(code), bytes)
+
+
+def _index(**kw):
+    d = IndexDesc(FAKE, FAKE, None, FAKE, FAKE, None, 1, 1, 1, 4, 64, 128, 1000, 1, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(w=None), NULL), (dict(q_pos=None), NULL),
+    (dict(S=0), SHAPE), (dict(n_q=0), SHAPE), (dict(H=0), SHAPE), (dict(H=129), SHAPE),
+    (dict(D=100), SHAPE), (dict(D=512), SHAPE), (dict(n_units=0), SHAPE),
+    (dict(c=0), PARAM), (dict(hadamard_q=2), PARAM), (dict(hadamard_q=1, D=64), SHAPE),
+    (dict(q_dtype=3), DTYPE), (dict(k_dtype=7), DTYPE),
+    (dict(k_dtype=3), NULL),                      # fp8 keys need a scale
+    (dict(k_scale=FAKE), PARAM),                  # a scale without fp8 keys
+    (dict(q=FAKE + 4), ALIGN), (dict(k=FAKE + 8), ALIGN),
+])
+def test_index_scores_rejects(kw, code):
+    L = dsa.lib()
+    assert L.dsa_index_scores(ctypes.byref(_index(**kw)), ctypes.c_void_p(FAKE), None) == code
+    assert L.dsa_index_scores(None, ctypes.c_void_p(FAKE), None) == NULL
+    assert L.dsa_index_scores(ctypes.byref(_index()), None, None) == NULL
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_pos=None), NULL), (dict(S=0), SHAPE), (dict(n_units=0), SHAPE),
+    (dict(top_k=0), PARAM), (dict(c=0), PARAM), (dict(c=3, top_k=64), PARAM),
+    (dict(n_sink=-1), PARAM), (dict(n_sink=65), PARAM), (dict(c=4, n_sink=1), PARAM),
+])
+def test_topk_rejects(kw, code):
+    L = dsa.lib()
+    d = TopkDesc(FAKE, None, 1, 4, 1000, 64, 1, 0, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    assert L.dsa_topk(ctypes.c_void_p(FAKE), ctypes.byref(d), ctypes.c_void_p(FAKE), None, 0, None) == code
+
+
+@no_gpu
+def test_topk_workspace_rule():
+    L = dsa.lib()
+    short = TopkDesc(FAKE, None, 1, 4096, 4096, 2048, 1, 0, 0)
+    long = TopkDesc(FAKE, None, 8, 1, 131072, 2048, 1, 0, 0)
+    assert L.dsa_topk_workspace_bytes(ctypes.byref(short)) == 0
+    need = L.dsa_topk_workspace_bytes(ctypes.byref(long))
+    assert need >= 8 * 131072 * 8
+    assert L.dsa_topk(ctypes.c_void_p(FAKE), ctypes.byref(long), ctypes.c_void_p(FAKE), None, need,
+                      None) == WORKSPACE
+    assert L.dsa_topk(ctypes.c_void_p(FAKE), ctypes.byref(long), ctypes.c_void_p(FAKE),
+                      ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+
+
+@no_gpu
+def test_block_pool_rejects():
+    L = dsa.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert L.dsa_block_pool(None, 1, 1, 100, 128, 4, f, None) == NULL
+    assert L.dsa_block_pool(f, 3, 1, 100, 128, 4, f, None) == DTYPE
+    assert L.dsa_block_pool(f, 1, 0, 100, 128, 4, f, None) == SHAPE
+    assert L.dsa_block_pool(f, 1, 1, 100, 128, 0, f, None) == PARAM
+
+
+def _mla(**kw):
+    d = AttnDesc(FAKE, FAKE, FAKE, 1000 * 576, 576, 576, 1000 * 576, 576, 576, FAKE, None,
+                 1, 0, 1, 4, 128, 1, 576, 512, 1000, 64, 1, 0.0, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(q_pos=None), NULL), (dict(S=0), SHAPE), (dict(Hq=100), UNSUP),
+    (dict(Hkv=3), SHAPE), (dict(n_kv=0), SHAPE), (dict(o_dtype=2), DTYPE), (dict(dtype=2), DTYPE),
+    (dict(c=0), PARAM), (dict(k_sel=0), SHAPE), (dict(c=4, k_sel=5000), SHAPE),
+    (dict(v=FAKE + 1024), UNSUP),                 # MLA values must alias the latent rows
+    (dict(Dk=64, Dv=64), UNSUP), (dict(k_tok_stride=-1), SHAPE),
+    (dict(k_tok_stride=577, v_tok_stride=577), ALIGN), (dict(q=FAKE + 2), ALIGN),
+])
+def test_sparse_attn_rejects(kw, code):
+    L = dsa.lib()
+    d = _mla(**kw)
+    assert L.dsa_sparse_attn(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, 0,
+                             None) == code
+
+
+@no_gpu
+def test_sparse_attn_workspace_rule():
+    L = dsa.lib()
+    decode = _mla(S=8, n_q=1, n_kv=131072, k_sel=2048)
+    need = L.dsa_sparse_attn_workspace_bytes(ctypes.byref(decode), 0)
+    assert need > 0            # few rows: the stream is split and merged
+    assert L.dsa_sparse_attn(ctypes.byref(decode), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), need - 4, None) == WORKSPACE
+    prefill = _mla(S=1, n_q=4096, n_kv=4096, k_sel=2048)
+    assert L.dsa_sparse_attn_workspace_bytes(ctypes.byref(prefill), 0) == 0
+
+
+def _fwd(**kw):
+    d = ForwardDesc(FAKE, FAKE, None, FAKE, 1, 1, 64, 128, 2048, 1, 0, 0,
+                    FAKE, FAKE, FAKE, 4096 * 576, 576, 576, 4096 * 576, 576, 576,
+                    1, 0, 128, 1, 576, 512, 0.0, 0, 1, 4096, 4096, FAKE, None, FAKE, None, None, None)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), NULL), (dict(w=None), NULL), (dict(top_k=0), PARAM),
+    (dict(c=64, top_k=100), PARAM), (dict(c=64, n_sink=1), PARAM), (dict(n_sink=4096), PARAM),
+    (dict(c=64, k_idx_dtype=3, k_scale=FAKE), DTYPE), (dict(k_idx_dtype=3), NULL),
+    (dict(H=200), SHAPE), (dict(Hq=96, Dk=128, Dv=128, Hkv=1, v=FAKE), UNSUP),
+    (dict(scores_out=FAKE + 4), ALIGN),
+])
+def test_forward_rejects(kw, code):
+    L = dsa.lib()
+    d = _fwd(**kw)
+    assert L.dsa_forward(ctypes.byref(d), ctypes.c_void_p(FAKE), 1 << 40, None) == code
+
+
+@no_gpu
+def test_forward_workspace_covers_intermediates():
+    L = dsa.lib()
+    prefill = _fwd()
+    need = L.dsa_forward_workspace_bytes(ctypes.byref(prefill))
+    assert need >= 4096 * 4096 * 4 + 4096 * 2048 * 4   # scores + idx
+    assert L.dsa_forward(ctypes.byref(prefill), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+    assert L.dsa_forward(ctypes.byref(prefill), None, need, None) == WORKSPACE
