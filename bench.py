@@ -1,0 +1,239 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one dsa_forward call over the whole batch of the workload: indexer
+scores -> top-k -> sparse attention (block pooling first in block mode).
+Inputs are seeded synthetic tensors already resident in HBM.  Prints one JSON
+line.  The default workload is the 4096-token DSA prefill (128-head MLA
+attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1..5]
+                    [--no-cpu-baseline] [--calib-copy]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: DSA prefill)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run one 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ algorithmic work
+
+def work_model(wl, q_pos, kv_len):
+    """Per-phase algorithmic flops and HBM bytes of one step (what the method
+    must compute and move), from the positions and sizes of the workload."""
+    qp = q_pos.astype(np.int64)
+    kv = np.repeat(kv_len.astype(np.int64)[:, None], wl.n_q, axis=1)
+    n_vis = np.clip(np.minimum(qp + 1, kv), 0, None)                 # visible tokens per query
+    units = n_vis // wl.c                                             # visible scored units
+    k_out = wl.top_k // wl.c
+    if wl.c > 1:
+        sel = np.minimum(units, k_out) * wl.c + (n_vis - units * wl.c)  # blocks + tail
+    else:
+        sel = np.minimum(units, k_out)
+    pairs_score = int(units.sum())
+    pairs_attn = int(sel.sum())
+    esz = {"torch.bfloat16": 2, "torch.float16": 2, "torch.float32": 4, "torch.float8_e4m3fn": 1}
+    kb = esz[str(wl.k_dtype)]
+    qb = esz[str(wl.q_dtype)]
+    ab = esz[str(wl.a_dtype)]
+    rows = wl.S * wl.n_q
+    n_units_row = wl.n_kv // wl.c
+    d = {}
+    # S1 block pooling: read raw keys, write pooled keys
+    d["pool"] = dict(flops=0, bytes=(wl.S * wl.n_kv * wl.D * kb + wl.S * n_units_row * wl.D * 4) if wl.c > 1 else 0)
+    # S2 scores: one dot of D per head per visible unit; q, keys (+scales), w read, scores written
+    key_bytes = wl.S * n_units_row * wl.D * (4 if wl.c > 1 else kb)
+    if wl.k_dtype.is_floating_point and kb == 1:
+        key_bytes += wl.S * n_units_row * 4
+    d["scores"] = dict(flops=2 * pairs_score * wl.H * wl.D,
+                       bytes=rows * wl.H * wl.D * qb + key_bytes + rows * wl.H * 4 + pairs_score * 4)
+    # S3 top-k: visible scores read, index rows written
+    d["topk"] = dict(flops=0, bytes=pairs_score * 4 + rows * k_out * 4)
+    # S5 attention: q.k over Dk and p.v over Dv per head per selected token; Q read, the
+    # selected K/V rows read (each distinct row once), O written
+    if wl.attn == "mla":
+        kv_row_bytes = wl.Dk * ab
+        distinct = wl.S * wl.n_kv * kv_row_bytes if wl.n_q > 1 else pairs_attn * kv_row_bytes
+    else:
+        kv_row_bytes = wl.Hkv * (wl.Dk + wl.Dv) * ab
+        distinct = wl.S * wl.n_kv * kv_row_bytes if wl.n_q > 1 else pairs_attn * kv_row_bytes
+    d["attn"] = dict(flops=2 * pairs_attn * wl.Hq * (wl.Dk + wl.Dv),
+                     bytes=rows * wl.Hq * wl.Dk * ab + distinct + rows * wl.Hq * wl.Dv * 4)
+    return d, pairs_score, pairs_attn
+
+
+def compute_dtype(wl):
+    if wl.a_dtype.__repr__() == "torch.float32":
+        return "f32"
+    return "bf16"
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(wl, x, budget_s):
+    """Times the CPU oracle on a bounded sample of query rows of the same
+    workload (rows evenly spread over the batch, so the causal cost mix is
+    kept), and scales to query tokens/s."""
+    import torch
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:   # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    f = O.to_f64
+    rows = [(s, i) for s in range(wl.S) for i in range(wl.n_q)]
+    # bit-reversed order: every prefix of it is spread evenly over the batch
+    nb = max(1, (len(rows) - 1).bit_length())
+    order = sorted(range(len(rows)), key=lambda r: int(format(r, f"0{nb}b")[::-1], 2))
+    sample = [rows[r] for r in order]
+    # inputs the sampled rows read, converted once outside the timed region
+    k_idx = [f(x["k_idx"][s:s + 1]) for s in range(wl.S)]
+    k_scale = [None if x["k_scale"] is None else f(x["k_scale"][s:s + 1]) for s in range(wl.S)]
+    K = [f(x["K"][s:s + 1]) for s in range(wl.S)]
+    V = [f(x["V"][s:s + 1]) for s in range(wl.S)]
+    kv = x["kv_len"].cpu().numpy()
+    done, t_total = 0, 0.0
+    for s, i in sample:
+        qi = f(x["q_idx"][s:s + 1, i:i + 1])
+        w = f(x["w"][s:s + 1, i:i + 1])
+        Q = f(x["Q"][s:s + 1, i:i + 1])
+        qp = x["q_pos"][s:s + 1, i:i + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        O.forward(Q, K[s], V[s], qi, k_idx[s], w, wl.top_k, wl.c, qp, kv[s:s + 1], k_scale[s],
+                  wl.n_sink if wl.c == 1 else 0, wl.scale, wl.hadamard_q)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total > budget_s and done >= 4:
+            break
+    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(rows)} query rows of the {wl.name} batch, taken in bit-reversed order "
+                      f"(evenly spread), numpy float64 oracle, {t_total:.1f} s"}
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_top_attention_indexer_amd as dsa
+    from sparse_top_attention_indexer_amd import inputs
+
+    wl = inputs.preset(args.config)
+    dev = "cuda"
+    x = inputs.generate(wl, device=dev)
+    kw = dict(k_scale=x["k_scale"], n_sink=wl.n_sink if wl.c == 1 else 0, scale=wl.scale,
+              hadamard_q=wl.hadamard_q, kv_len=x["kv_len"])
+    out = torch.empty((wl.S, wl.n_q, wl.Hq, wl.Dv), device=dev, dtype=torch.float32)
+    nbytes = dsa.forward_workspace_bytes(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k,
+                                         wl.c, x["q_pos"], **kw)
+    ws = torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
+    ev = [[dsa.Event() for _ in range(5)] for _ in range(args.steps)]
+
+    def step(events=None):
+        dsa.forward(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k, wl.c, x["q_pos"],
+                    out=out, workspace=ws, phase_events=events, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    # per-phase times from the HIP events recorded on the library's stream
+    names = ["scores", "topk", "attn", "combine"]
+    phase_ms = {n_: 0.0 for n_ in names}
+    for k in range(args.steps):
+        for j, n_ in enumerate(names):
+            phase_ms[n_] += ev[k][j].elapsed_ms(ev[k][j + 1]) / args.steps
+
+    work, pairs_score, pairs_attn = work_model(wl, x["q_pos"].cpu().numpy(), x["kv_len"].cpu().numpy())
+    if wl.c > 1:   # pooling runs inside the first phase with the scores
+        work["scores"] = {"flops": work["scores"]["flops"], "bytes": work["scores"]["bytes"] + work["pool"]["bytes"]}
+    cdt = compute_dtype(wl)
+    per_phase = {}
+    for n_ in ("scores", "topk", "attn"):
+        t = max(phase_ms[n_] * 1e-3, 1e-12)
+        fl, by = work[n_]["flops"], work[n_]["bytes"]
+        peak_f = PEAK["f16" if (n_ == "scores" and wl.k_dtype != torch.bfloat16 and cdt != "f32") else cdt]
+        if n_ == "scores" and cdt == "f32":
+            peak_f = PEAK["f32"]
+        t_f, t_b = fl / peak_f, by / PEAK_HBM
+        bound = "mfma" if t_f >= t_b else "hbm"
+        per_phase[n_] = dict(ms=phase_ms[n_], flops=fl, bytes=by, bound=bound,
+                             frac=(t_f if bound == "mfma" else t_b) / t, peak=peak_f if bound == "mfma" else PEAK_HBM)
+    dom = max(("scores", "topk", "attn"), key=lambda n_: phase_ms[n_])
+    ph = per_phase[dom]
+    t_dom = ph["ms"] * 1e-3
+    if ph["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": ph["flops"] / t_dom / 1e12, "peak": ph["peak"] / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": ph["bytes"] / t_dom / 1e9, "peak": ph["peak"] / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = {"scores": "score_mfma_kernel", "topk": "topk kernels", "attn":
+                      {"mla": "attn_mla_kernel", "gqa": "attn_gqa_kernel", "f32": "attn_f32_kernel"}[wl.attn]}[dom]
+    roof["launch_ms"] = ph["ms"]
+
+    q_tokens = wl.S * wl.n_q
+    value = q_tokens / (ms_step * 1e-3)
+    line = {
+        "metric": "query tokens/s + indexer keys scored/s (1 GPU), % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "query tokens/s",
+        "keys_scored_per_s": pairs_score / (ms_step * 1e-3),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cdt, "data": "synthetic",
+        "config": {"workload": wl.name, "sequences": wl.S, "queries_per_sequence": wl.n_q, "cached_keys": wl.n_kv,
+                   "indexer_heads": wl.H, "indexer_dim": wl.D, "indexer_key_dtype": str(wl.k_dtype).split(".")[1],
+                   "top_k": wl.top_k, "compress_ratio": wl.c, "n_sink": wl.n_sink, "attention": wl.attn,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "dk": wl.Dk, "dv": wl.Dv,
+                   "scored_pairs": pairs_score, "attended_pairs": pairs_attn},
+        "phases_ms": {k_: round(v_, 5) for k_, v_ in phase_ms.items()},
+        "phase_roofline_frac": {k_: round(v_["frac"], 4) for k_, v_ in per_phase.items()},
+        "roofline": roof,
+    }
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
