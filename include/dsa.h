@@ -170,7 +170,7 @@ int dsa_block_pool(const void* k_raw, int32_t dtype /* F32 | BF16 | F16 */,
  * Rows with an empty T(i) are written as zeros.
  * Supported families (DSA_ERR_UNSUPPORTED otherwise):
  *  - F32:  Q/K/V f32, Dk, Dv <= 256, any Hq multiple of Hkv;
- *  - MLA:  BF16, Hkv == 1, Dk == 576, Dv == 512, Hq a multiple of 32, V
+ *  - MLA:  BF16, Hkv == 1, Dk == 576, Dv == 512, Hq a multiple of 16, V
  *          aliasing the first 512 columns of K (same pointer and strides);
  *  - GQA:  BF16, Dk == Dv == 128, Hq / Hkv <= 16.
  * ---------------------------------------------------------------------- */

@@ -63,8 +63,9 @@ int attn_family(const dsa_attn_desc* d) {
     return ATTN_F32;
   }
   if (d->dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if (d->Hkv == 1 && d->Dk == 576 && d->Dv == 512 && d->Hq % 32 == 0 && d->v == d->k &&
-      d->v_seq_stride == d->k_seq_stride && d->v_tok_stride == d->k_tok_stride)
+  if (d->Hkv == 1 && d->Dk == 576 && d->Dv == 512 && d->Hq % 16 == 0 && d->v == d->k &&
+      d->v_seq_stride == d->k_seq_stride && d->v_tok_stride == d->k_tok_stride &&
+      d->n_kv * d->k_tok_stride * 2 < (int64_t(1) << 32))   // 32-bit row offsets within a sequence
     return ATTN_MLA;
   if (d->Dk == 128 && d->Dv == 128 && d->Hq / d->Hkv <= 16) return ATTN_GQA;
   return DSA_ERR_UNSUPPORTED;

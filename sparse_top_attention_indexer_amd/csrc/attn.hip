@@ -115,7 +115,7 @@ constexpr int KT_ROW = KT_SLOTS * 16;              // 1184 B: rows start 8 banks
 constexpr int KT_BYTES = TILE * KT_ROW;            // one gathered tile
 constexpr int KT_INSTR = TILE * KT_SLOTS / 64;     // wave-wide 1 KB loads per tile (37)
 constexpr int MLA_WAVES = 8;
-constexpr size_t MLA_LDS = 2 * KT_BYTES + MLA_WAVES * 4 * 64 * 16 + 3 * TILE * 4 + 64 + MAX_BLOCKS * 4;
+constexpr size_t MLA_LDS = 2 * KT_BYTES + 3 * TILE * 4 + 64 + MAX_BLOCKS * 4;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -141,27 +141,28 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // columns (transposing reads) both spread over all 32 banks.
 __device__ __forceinline__ int kt_slot(int r, int c) { return c ^ ((r >> 2) & 1); }
 
-// One workgroup = one query row x one stream chunk x 128 heads, 8 waves.
-// Wave w: head block hb = w & 3 (32 heads), half dh = w >> 2.  Per tile of 32
+// One workgroup = one query row x one stream chunk x 128 heads, 8 waves; wave
+// w owns heads 16 w .. 16 w + 15 and all 576 contraction dims.  Per tile of 32
 // gathered latent rows:
-//   S^T partial = K_tile[:, 288 dh : 288 dh + 288] . Q^T (same dims) on
-//                 32x32x16 MFMAs, Q in registers; the two halves of a head
-//                 block add their partials through LDS (both get the same sum)
-//   online softmax over the 32 keys of each head (exact running max)
-//   O^T[256 dh : 256 dh + 256] += V^T . P^T: V^T fragments are read straight
-//                 from the key-major tile with the transposing LDS read, P^T
-//                 comes from S^T's accumulator layout rounded to bf16
+//   S^T (32 keys x 16 heads) = K_tile . Q^T on 16x16x32 MFMAs, K fragments
+//       read from the LDS tile, Q in registers
+//   online softmax over the 32 keys of each head (in-lane + two swaps); the
+//       running max is only raised when it grows by more than 2^8 in weight,
+//       and the weights enter the PV product as a bf16 high part plus a bf16
+//       residual, so they stay exact to ~2^-17 even when they exceed 1
+//   O^T (512 dims x 16 heads) += V^T . P^T: V^T fragments come straight from
+//       the key-major tile through the transposing LDS read; P^T is the S^T
+//       accumulator layout
 // Tiles are gathered with direct global -> LDS loads, double buffered.
 __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t s_raw[];
   uint8_t* s_kb = s_raw;                                                    // 2 tiles
-  f32x4_t* s_x = reinterpret_cast<f32x4_t*>(s_raw + 2 * KT_BYTES);          // [wave][4][64]
-  int32_t* s_tok = reinterpret_cast<int32_t*>(s_raw + 2 * KT_BYTES + MLA_WAVES * 4 * 64 * 16);  // [3][32]
+  int32_t* s_tok = reinterpret_cast<int32_t*>(s_raw + 2 * KT_BYTES);        // [3][32]
   uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_tok + 3 * TILE);
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31, h2 = lane >> 5;
-  const int hb = wid & 3, dh = wid >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, quad = lane >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int64_t row = blockIdx.x / p.n_split;
   const int sp = blockIdx.x % p.n_split;
   const int s = static_cast<int>(row / p.n_q);
@@ -170,21 +171,20 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   split_range(p, sp, si.len, &p0, &p1);
   const int n_tiles = static_cast<int>((p1 - p0 + TILE - 1) / TILE);
 
-  const int head0 = blockIdx.y * 128 + hb * 32;
-  const bool hvalid = head0 < p.Hq;   // Hq is a multiple of 32
-  const int head = head0 + n;
+  const int head0 = blockIdx.y * 128 + wid * 16;
+  const bool hvalid = head0 < p.Hq;   // Hq is a multiple of 16
+  const int head = head0 + col;
 
   u32x4_t qf[18];
   {
     const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (hvalid ? head : 0)) * MLA_DK;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks)
-      qf[ks] = hvalid ? *reinterpret_cast<const u32x4_t*>(qr + 16 * (18 * dh + ks) + 8 * h2)
-                      : u32x4_t{0u, 0u, 0u, 0u};
+      qf[ks] = hvalid ? *reinterpret_cast<const u32x4_t*>(qr + 32 * ks + 8 * quad) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  f32x16_t o[8];
+  f32x4_t o[32];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x16_t{};
+  for (int db = 0; db < 32; ++db) o[db] = f32x4_t{};
   float m_run = NEG_INF, l_run = 0.f;
   const float c2 = p.scale_log2;
   const uint16_t* kseq = static_cast<const uint16_t*>(p.k) + s * p.k_seq;
@@ -192,150 +192,154 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   // gather of one tile: 37 wave-instructions of 64 x 16 B; lane L of
   // instruction I fills physical slot 64 I + L of the tile (pad slots reload
   // the row's first chunk)
+  constexpr int MAXI = (KT_INSTR + MLA_WAVES - 1) / MLA_WAVES;   // 5
+  const uint32_t kb_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_kb));
+  const char* kseq_b = reinterpret_cast<const char*>(kseq);
+  const uint32_t pitch = static_cast<uint32_t>(p.k_tok) * 2u;   // bytes per token row (< 4 GiB per sequence)
   auto issue = [&](int t, int buf) {
     const int32_t* tk = s_tok + (t % 3) * TILE;
-    uint8_t* dst = s_kb + buf * KT_BYTES;
-    for (int I = wid; I < KT_INSTR; I += MLA_WAVES) {
-      const int q = 64 * I + lane;
-      const int r = q / KT_SLOTS, pc = q - KT_SLOTS * r;
-      const int c = pc < KT_CHUNKS ? kt_slot(r, pc) : 0;
-      const int64_t tok = tk[r];
-      const uint16_t* src = kseq + (tok >= 0 ? tok : 0) * p.k_tok + 8 * c;
-      dma16(src, __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-                     reinterpret_cast<uintptr_t>((lds_void_t*)(dst + 1024 * I)))));
+    // recomputed at every call: keeping these per-lane constants live across
+    // the tile loop would cost registers the MFMA operands need
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+      const int I = wid + MLA_WAVES * k;
+      if (I < KT_INSTR) {
+        const int q = 64 * I + ln;
+        const int r = q / KT_SLOTS, pc = q - KT_SLOTS * r;
+        const int c = pc < KT_CHUNKS ? kt_slot(r, pc) : 0;
+        const int32_t tok = tk[r];
+        const uint32_t off = static_cast<uint32_t>(tok >= 0 ? tok : 0) * pitch + 16u * static_cast<uint32_t>(c);
+        dma16(kseq_b + off, __builtin_amdgcn_readfirstlane(kb_lds + buf * KT_BYTES + 1024 * I));
+      }
     }
   };
-  if (tid < TILE) s_tok[tid] = static_cast<int32_t>(p0 + tid < p1 ? stream_token(p, row, si, s_blk, p0 + tid) : -1);
+  // token ids run two tiles ahead of their use: lane < 32 of wave 0 loads the
+  // raw idx entry of tile t + 2 (from a clamped position, unconditionally, so
+  // nothing waits for it) while tile t is computed, and validates it when it
+  // stores it one tile later
+  const bool token_mode = p.idx != nullptr && p.c == 1;
+  auto fetch = [&](int64_t pos) -> int32_t {
+    return token_mode ? p.idx[row * p.k_sel + (pos < p1 ? pos : p1 - 1)] : 0;
+  };
+  auto store_token = [&](int slot, int64_t pos, int32_t raw) {
+    int32_t t = -1;
+    if (pos < p1) {
+      if (token_mode) t = (raw >= 0 && raw < si.n_vis) ? raw : -1;
+      else t = static_cast<int32_t>(stream_token(p, row, si, s_blk, pos));
+    }
+    s_tok[slot * TILE + tid] = t;
+  };
+  int32_t pending = 0;
+  if (tid < TILE && n_tiles > 0) {
+    store_token(0, p0 + tid, fetch(p0 + tid));
+    pending = fetch(p0 + TILE + tid);
+  }
   __syncthreads();
   if (n_tiles > 0) issue(0, 0);
 
-  // transposing-read lane roles (see the PV step)
-  const int tg = lane >> 4, ti = lane & 15;
-  const int tr_m = ti >> 2, tr_r = ti & 3, tr_hh = tg >> 1, tr_gp = tg & 1;
+  // per-lane byte offsets inside a tile (the swizzle bit of a row depends on
+  // row bits 2, which the 16-row and 4-row groups below never change)
+  const int sw = (col >> 2) & 1;
+  const uint32_t s_off = col * KT_ROW + 16 * (quad ^ sw);                   // S: row col (+16 mb), chunk 4 ks + quad
+  const int tm = col >> 2, tr = col & 3;
+  const uint32_t v_off = (4 * quad + tm) * KT_ROW + 16 * ((tr >> 1) ^ (quad & 1)) + 8 * (tr & 1);  // PV
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles && tid < TILE) {
-      const int64_t pos = p0 + static_cast<int64_t>(t + 1) * TILE + tid;
-      s_tok[((t + 1) % 3) * TILE + tid] = static_cast<int32_t>(pos < p1 ? stream_token(p, row, si, s_blk, pos) : -1);
-    }
+    if (tid < TILE) store_token((t + 1) % 3, p0 + static_cast<int64_t>(t + 1) * TILE + tid, pending);
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this thread's part of tile t has landed
     __syncthreads();                      // tile t complete; tile t-1 no longer read
     if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
+    if (tid < TILE) pending = fetch(p0 + static_cast<int64_t>(t + 2) * TILE + tid);
+    __builtin_amdgcn_sched_barrier(0);
 
+    // live entries of the tile as a bit mask (uniform)
     const int32_t* tk = s_tok + (t % 3) * TILE;
-    bool any = false;
-#pragma unroll
-    for (int r = 0; r < TILE; ++r) any |= tk[r] >= 0;
-    if (!any) continue;   // uniform across the workgroup
+    const uint64_t live = __ballot(lane < TILE && tk[lane] >= 0) & 0xffffffffull;
+    if (live == 0 || !hvalid) continue;
 
     const uint8_t* kt = s_kb + buf * KT_BYTES;
-    f32x16_t sacc = f32x16_t{};
-    {
-      // row n, data chunk 2 (18 dh + ks) + h2: slot = that ^ ((n >> 2) & 1)
-      const uint8_t* sb = kt + n * KT_ROW + 16 * (36 * dh + (h2 ^ ((n >> 2) & 1)));
+    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(sb + 32 * ks);
-        sacc = mfma32x32x16_bf16(a, qf[ks], sacc);
+    for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + s_off + mb * 16 * KT_ROW + 64 * ks);
+        sacc[mb] = mfma16x16x32_bf16(a, qf[ks], sacc[mb]);
       }
     }
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4)
-      s_x[(wid * 4 + j4) * 64 + lane] = f32x4_t{sacc[4 * j4], sacc[4 * j4 + 1], sacc[4 * j4 + 2], sacc[4 * j4 + 3]};
-    barrier_lds_only();   // the next tile's global -> LDS loads stay in flight
-    float sv[16];
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const f32x4_t q4 = s_x[((wid ^ 4) * 4 + j4) * 64 + lane];
-      sv[4 * j4] = sacc[4 * j4] + q4[0];
-      sv[4 * j4 + 1] = sacc[4 * j4 + 1] + q4[1];
-      sv[4 * j4 + 2] = sacc[4 * j4 + 2] + q4[2];
-      sv[4 * j4 + 3] = sacc[4 * j4 + 3] + q4[3];
-    }
+    // accumulator (mb, j) holds key 16 mb + 4 quad + j of head `col`
+    float sv[8];
     float tmax = NEG_INF;
+    const uint32_t lm = static_cast<uint32_t>(live) >> (4 * quad);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kr_ = 8 * (j >> 2) + 4 * h2 + (j & 3);
-      if (tk[kr_] < 0) sv[j] = NEG_INF;
+    for (int j = 0; j < 8; ++j) {
+      sv[j] = ((lm >> (16 * (j >> 2) + (j & 3))) & 1u) ? sacc[j >> 2][j & 3] : NEG_INF;
       tmax = fmaxf(tmax, sv[j]);
     }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // exact running max: the key that sets it enters with weight exactly 1
     if (m_run == NEG_INF) {
       m_run = tmax;
-    } else if (tmax > m_run) {
+    } else if ((tmax - m_run) * c2 > 8.f) {
       const float alpha = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
       m_run = tmax;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      for (int db = 0; db < 32; ++db) o[db] *= alpha;
     }
-    // weights as a bf16 high part plus a bf16 residual: the two MFMAs over the
-    // same V fragment keep the weights to ~2^-17 relative, so large value rows
-    // (outlier tokens) do not amplify a 2^-9 weight rounding
-    const float mb = m_run * c2;
-    uint32_t pk[8], pl[8];
+    const float mb_ = m_run * c2;
+    uint32_t pk[4], pl[4];
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float a = __builtin_amdgcn_exp2f(fmaf(sv[j], c2, -mb));
-      const float b = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], c2, -mb));
-      pk[j >> 1] = pack_bf16x2(a, b);
-      pl[j >> 1] = pack_bf16x2(a - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] & 0xffffu)),
-                               b - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] >> 16)));
-      psum += a + b;
+    for (int j = 0; j < 8; j += 2) {
+      const float x0 = __builtin_amdgcn_exp2f(fmaf(sv[j], c2, -mb_));
+      const float x1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], c2, -mb_));
+      pk[j >> 1] = pack_bf16x2(x0, x1);
+      pl[j >> 1] = pack_bf16x2(x0 - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] & 0xffffu)),
+                               x1 - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] >> 16)));
+      psum += x0 + x1;
     }
+    psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
-    const u32x4_t pb[2] = {u32x4_t{pk[0], pk[1], pk[2], pk[3]}, u32x4_t{pk[4], pk[5], pk[6], pk[7]}};
-    const u32x4_t pr[2] = {u32x4_t{pl[0], pl[1], pl[2], pl[3]}, u32x4_t{pl[4], pl[5], pl[6], pl[7]}};
-    // V^T fragment of MFMA kk: lane (16 g + j) needs dim (16 (g & 1) + j) of its
-    // 32-dim block for keys 16 kk + 4 (g >> 1) + {0..3} (slots 0..3) and the same
-    // plus 8 (slots 4..7).  Within each 16-lane group the transposing read hands
-    // lane j element j % 4 of the 8-byte rows addressed by lanes j / 4 + 4 m,
-    // so lane 4 m + r addresses key (.. + m), dims 4 r .. 4 r + 3 of the group.
-    {
-      // rows 16 kk + 4 tr_hh + tr_m (+ 8) all have (row >> 2) & 1 == tr_hh; data chunk
-      // 32 dh + 4 db + 2 tr_gp + (tr_r >> 1), byte 8 (tr_r & 1) inside it
-      const uint8_t* vb = kt + (4 * tr_hh + tr_m) * KT_ROW +
-                          16 * (32 * dh + ((2 * tr_gp + (tr_r >> 1)) ^ tr_hh)) + 8 * (tr_r & 1);
+    // P^T slot (quad, j) <-> key 4 quad + j (j < 4) / 16 + 4 quad + j - 4 (j >= 4)
+    const u32x4_t pb = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+    const u32x4_t pr = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+    // V^T fragment of dim block db: lane (quad, j) needs dim 16 db + j for keys
+    // 4 quad + {0..3} and 16 + 4 quad + {0..3}.  The transposing read hands lane
+    // j of a 16-lane group element j % 4 of the rows addressed by lanes
+    // j / 4 + 4 m, so lane 4 m + r addresses key 4 quad + m, dims 16 db + 4 r.
+    const uint8_t* vb = kt + v_off;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint8_t* a0 = vb + 64 * db + 16 * kk * KT_ROW;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(const_cast<uint8_t*>(a0)));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)(const_cast<uint8_t*>(a0 + 8 * KT_ROW)));
-          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2v = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t va = u32x4_t{l2.x, l2.y, h2v.x, h2v.y};
-          o[db] = mfma32x32x16_bf16(va, pb[kk], o[db]);
-          o[db] = mfma32x32x16_bf16(va, pr[kk], o[db]);
-        }
-      }
+    for (int db = 0; db < 32; ++db) {
+      const uint8_t* a0 = vb + 32 * db;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(const_cast<uint8_t*>(a0)));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(const_cast<uint8_t*>(a0 + 16 * KT_ROW)));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2v = __builtin_bit_cast(u32x2_t, hi);
+      const u32x4_t va = u32x4_t{l2.x, l2.y, h2v.x, h2v.y};
+      o[db] = mfma16x16x32_bf16(va, pb, o[db]);
+      o[db] = mfma16x16x32_bf16(va, pr, o[db]);
     }
   }
   if (!hvalid) return;
 
+  // accumulator (db, j) holds dim 16 db + 4 quad + j of head `col`
   if (p.n_split == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t ob = (row * p.Hq + head) * MLA_DV + 256 * dh;
+    const int64_t ob = (row * p.Hq + head) * MLA_DV;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        store4(p.out, p.o_dtype, ob + 32 * db + 8 * q4 + 4 * h2, o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv,
-               o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+    for (int db = 0; db < 32; ++db)
+      store4(p.out, p.o_dtype, ob + 16 * db + 4 * quad, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+             o[db][3] * inv);
   } else {
     float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * (MLA_DV + 2);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4_t*>(pp + 256 * dh + 32 * db + 8 * q4 + 4 * h2) =
-            f32x4_t{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
-    if (dh == 0 && h2 == 0) {
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * quad) = f32x4_t{o[db][0], o[db][1], o[db][2], o[db][3]};
+    if (quad == 0) {
       pp[MLA_DV] = m_run;
       pp[MLA_DV + 1] = l_run;
     }
