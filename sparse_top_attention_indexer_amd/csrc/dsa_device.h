@@ -64,7 +64,9 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4
 
 // Packs two floats as bf16 (low half = a) / f16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));   // one v_cvt_pk_bf16_f32
 }
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_f16(a)) | (static_cast<uint32_t>(f32_to_f16(b)) << 16);

@@ -99,6 +99,8 @@ struct AttnParams {
   int32_t family;        // ATTN_F32 / ATTN_MLA / ATTN_GQA
 };
 enum { ATTN_F32 = 0, ATTN_MLA = 1, ATTN_GQA = 2 };
+// Block-mode list length (blocks per row) the MLA kernel keeps in LDS.
+constexpr int MLA_MAX_BLOCKS = 1024;
 // Split policy and workspace; identical for dense and sparse calls whose
 // effective list length min(L, n_kv) agrees (keeps dense == sparse bitwise).
 void attn_plan(AttnParams& p, int64_t list_len);
