@@ -171,7 +171,9 @@ int dsa_block_pool(const void* k_raw, int32_t dtype /* F32 | BF16 | F16 */,
  * Supported families (DSA_ERR_UNSUPPORTED otherwise):
  *  - F32:  Q/K/V f32, Dk, Dv <= 256, any Hq multiple of Hkv;
  *  - MLA:  BF16, Hkv == 1, Dk == 576, Dv == 512, Hq a multiple of 16, V
- *          aliasing the first 512 columns of K (same pointer and strides);
+ *          aliasing the first 512 columns of K (same pointer and strides),
+ *          n_kv * k_tok_stride * 2 < 2^32, and in block mode k_sel <= 1024
+ *          (DSA_ERR_SHAPE otherwise);
  *  - GQA:  BF16, Dk == Dv == 128, Hq / Hkv <= 16.
  * ---------------------------------------------------------------------- */
 typedef struct {

@@ -84,6 +84,7 @@ int check_attn(const dsa_attn_desc* d, const int32_t* idx, const void* out) {
     return DSA_ERR_SHAPE;
   const int fam = attn_family(d);
   if (fam < 0) return fam;
+  if (fam == ATTN_MLA && idx && d->c > 1 && d->k_sel > MLA_MAX_BLOCKS) return DSA_ERR_SHAPE;
   if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(out)) return DSA_ERR_ALIGN;
   const size_t es = esize(d->dtype);
   if (fam != ATTN_F32) {

@@ -126,6 +126,8 @@ def _mla(**kw):
     (dict(q=None), NULL), (dict(q_pos=None), NULL), (dict(S=0), SHAPE), (dict(Hq=100), UNSUP),
     (dict(Hkv=3), SHAPE), (dict(n_kv=0), SHAPE), (dict(o_dtype=2), DTYPE), (dict(dtype=2), DTYPE),
     (dict(c=0), PARAM), (dict(k_sel=0), SHAPE), (dict(c=4, k_sel=5000), SHAPE),
+    (dict(c=4, k_sel=1025), SHAPE),               # MLA keeps at most 1024 block ids per row
+    (dict(n_kv=8 * 1024 * 1024), UNSUP),          # MLA row offsets within a sequence stay 32-bit
     (dict(v=FAKE + 1024), UNSUP),                 # MLA values must alias the latent rows
     (dict(Dk=64, Dv=64), UNSUP), (dict(k_tok_stride=-1), SHAPE),
     (dict(k_tok_stride=577, v_tok_stride=577), ALIGN), (dict(q=FAKE + 2), ALIGN),
