@@ -111,17 +111,13 @@ __device__ __forceinline__ void store4(void* out, int o_dtype, int64_t off, floa
 // ============================================================== MLA kernel ==
 
 constexpr int MLA_DK = 576, MLA_DV = 512;
-constexpr int MLA_WAVES = 4;                     // 32 query heads per wave
+constexpr int MLA_WAVES = 8;                     // 16 query heads each
 constexpr int KT_MAIN = TILE * 1024;             // dims 0..511 of the tile rows, 1 KB per row
 constexpr int KT_ROPE = TILE * 128;              // dims 512..575, 128 B per row
 constexpr int KT_BYTES = KT_MAIN + KT_ROPE;      // one gathered tile (36 KB)
-constexpr int KT_NBUF = 3;                       // tiles t (PV), t + 1 (S), t + 2 (in flight)
+constexpr int KT_NBUF = 3;                       // tiles read by the two wave groups + one in flight
 constexpr int TOK_RING = 1024;                   // validated token ids of 32 tiles
-constexpr int TOK_REFILL = TOK_RING / 2 / TILE;  // tiles per ring refill (16)
-constexpr int MLA_QL = 8;                        // 16-dim steps of Q kept in LDS (the last ones)
-constexpr int MLA_QR = 36 - MLA_QL;              // 16-dim steps of Q kept in registers
-constexpr int MLA_QBYTES = MLA_WAVES * MLA_QL * 64 * 16;
-constexpr size_t MLA_LDS = KT_NBUF * KT_BYTES + MLA_QBYTES + TOK_RING * 4 + 64 + MLA_MAX_BLOCKS * 4;
+constexpr size_t MLA_LDS = KT_NBUF * KT_BYTES + TOK_RING * 4 + 64 + MLA_MAX_BLOCKS * 4;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -138,55 +134,61 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 
 // XOR mask of the 16-byte slots of dims 0..511 in tile row r (1 KB rows).  16
-// aligned rows read at one chunk, or 4 aligned rows at 4 aligned neighbouring
-// chunks, land on 16 distinct slots mod 16; 8 aligned rows at one chunk, or 4
-// rows at 2 neighbouring chunks, on 8 distinct slots mod 8.  The 16-byte reads
-// of the key fragments and the transposing 8-byte reads of the value
+// aligned rows read at one chunk land on 16 distinct slots mod 16 (8 aligned
+// rows on 8 distinct slots mod 8), and 8 aligned rows read at an aligned pair
+// of chunks on 16 distinct slots mod 16 (4 rows on 8 mod 8).  The 16-byte
+// reads of the key fragments and the transposing 8-byte reads of the value
 // fragments are thus free of bank conflicts for 32 or 64 banks of 4 bytes.
 __device__ __forceinline__ uint32_t main_swz(uint32_t r) {
-  const uint32_t m = r & 3, b = (r >> 2) & 3;
-  return (b & 1) | ((m & 1) << 1) | ((m >> 1) << 2) | (((m & 1) ^ (b >> 1)) << 3);
+  r &= 15;
+  return 2 * (r & 7) + (((r >> 2) ^ (r >> 3)) & 1);
 }
 // Same for the 8 slots of dims 512..575 (128-byte rows): 16 aligned rows at one
 // chunk fall on distinct slots of a 256-byte bank period, 8 on distinct slots
 // of a 128-byte one.
 __device__ __forceinline__ uint32_t rope_swz(uint32_t r) { return ((r & 15) ^ ((r & 15) >> 3)) & 7; }
 
-// lane l receives the value of lane l ^ 32 (max / sum across the two key halves)
-__device__ __forceinline__ float swap_halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+// lane l receives the values of lanes l ^ 16 and l ^ 32 folded in: max / sum
+// over the four lanes that hold one head's 32 keys; every lane of the four
+// adds in the same order, so all hold the same result
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  // both halves add (lower, upper) in the same order: identical sums
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One workgroup = one query row x one stream chunk x 128 heads, 4 waves; wave
-// w owns heads 32 w .. 32 w + 31 and all 576 contraction dims.  Per tile of 32
+// One workgroup = one query row x one stream chunk x 128 heads, 8 waves; wave
+// w owns heads 16 w .. 16 w + 15 and all 576 contraction dims.  Per tile of 32
 // gathered latent rows:
-//   S^T (32 keys x 32 heads) = K_tile . Q^T on 32x32x16 MFMAs, K fragments
-//       read from the LDS tile, Q in registers
-//   online softmax over the 32 keys of each head (16 per lane + one lane
-//       swap); the running max is only raised when it grows by more than 2^8
+//   S^T (32 keys x 16 heads) = K_tile . Q^T on 16x16x32 MFMAs (two 16-key
+//       blocks), K fragments read from the LDS tile, Q in registers
+//   online softmax over the 32 keys of each head (8 per lane + two lane
+//       swaps); the running max is only raised when it grows by more than 2^8
 //       in weight, and the weights enter the PV product as a bf16 high part
 //       plus a bf16 residual, so they stay exact to ~2^-17 even above 1
-//   O^T (512 dims x 32 heads) += V^T . P^T: V^T fragments come straight from
+//   O^T (512 dims x 16 heads) += V^T . P^T: V^T fragments come straight from
 //       the key-major tile through the transposing LDS read; P^T is the S^T
 //       accumulator layout, so no data moves between lanes
-// Software pipeline: iteration t computes S of tile t + 1, then the PV
-// product of tile t, then the softmax of tile t + 1, so the exponentials and
-// packing overlap the PV matrix products; tile t + 2 is gathered meanwhile
-// with direct global -> LDS loads (three tile buffers).  Token ids of the
-// stream sit in an LDS ring of 32 tiles, refilled 16 tiles ahead.
-__global__ __launch_bounds__(256, 1) void attn_mla_kernel(AttnParams p) {
+// Work runs in segments separated by barriers: a wave computes the scores and
+// softmax of tile u in one segment and its PV products in the next, and
+// waves 4..7 run one segment behind waves 0..3, so on every SIMD (waves w and
+// w + 4) one wave's score products and exponentials overlap the other wave's
+// PV products.  Tiles are gathered with direct global -> LDS loads two
+// segments ahead (three tile buffers).  Token ids of the stream sit in an LDS
+// ring of 32 tiles, refilled 16 tiles ahead.
+__global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t s_raw[];
-  uint8_t* s_kb = s_raw;                                                       // KT_NBUF tiles
-  uint8_t* s_q = s_raw + KT_NBUF * KT_BYTES;                                   // Q fragments
-  int32_t* s_tok = reinterpret_cast<int32_t*>(s_q + MLA_QBYTES);               // token ring
+  uint8_t* s_kb = s_raw;                                                      // KT_NBUF tiles
+  int32_t* s_tok = reinterpret_cast<int32_t*>(s_raw + KT_NBUF * KT_BYTES);   // token ring
   uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_tok + TOK_RING);
-  int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);                    // MLA_MAX_BLOCKS
+  int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);                   // MLA_MAX_BLOCKS
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
@@ -213,331 +215,287 @@ __global__ __launch_bounds__(256, 1) void attn_mla_kernel(AttnParams p) {
     p1 = p0 + s_scr[8];
   }
   const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
-  auto token_at = [&](int64_t pos) __attribute__((always_inline)) -> int32_t {
-    return pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
-  };
-  for (int i = tid; i < TOK_RING; i += 64 * MLA_WAVES) s_tok[i] = token_at(p0 + i);
+  for (int i = tid; i < TOK_RING; i += 64 * MLA_WAVES)
+    s_tok[i] = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
 
-  const int r32 = lane & 31, h = lane >> 5;
-  const int head0 = blockIdx.y * 128 + wid * 32;
+  const int grp = wid >> 2;
+  const int col = lane & 15, q = lane >> 4;
+  const int head0 = blockIdx.y * 128 + wid * 16;
   const bool wvalid = head0 < p.Hq;   // Hq is a multiple of 16
-  const int head = head0 + r32;
-  const bool hvalid = head < p.Hq;
+  const int head = head0 + col;
 
-  // Q^T fragments: lane (head, h) holds dims 16 ks + 8 h .. + 7 (chunk 2 ks + h);
-  // steps ks < MLA_QR in registers, the others in LDS in fragment order (the
-  // registers are what the accumulators and the pipelined loads need most)
-  u32x4_t qf[MLA_QR];
-  u32x4_t* s_qw = reinterpret_cast<u32x4_t*>(s_q) + wid * MLA_QL * 64 + lane;
+  // Contraction step ks takes four 8-dim chunks, one per lane group q: for
+  // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
+  // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
+  // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
+  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk.
+  u32x4_t qf[18];
   {
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (hvalid ? head : 0)) * MLA_DK + 8 * h;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      const u32x4_t v = hvalid ? *reinterpret_cast<const u32x4_t*>(qr + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-      if (ks < MLA_QR) qf[ks] = v;
-      else s_qw[(ks - MLA_QR) * 64] = v;
+    for (int ks = 0; ks < 18; ++ks) {
+      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
+      qf[ks] = wvalid ? *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  f32x16_t o[16];
+  f32x4_t o[32];
 #pragma unroll
-  for (int db = 0; db < 16; ++db) o[db] = f32x16_t{};
+  for (int db = 0; db < 32; ++db) o[db] = f32x4_t{};
   float m_run = NEG_INF, l_run = 0.f;
   const float c2 = p.scale_log2;
 
   const uint32_t kb_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_kb));
   const char* kseq_b = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) + s * p.k_seq);
   const uint64_t pitch = static_cast<uint64_t>(p.k_tok) * 2u;   // bytes per token row
-  // Gather of tile u into buffer lb: wave w loads the 1 KB main parts of rows
-  // w, w + 4, ..., w + 28 (instruction k < 8: row w + 4 k, its token id read
-  // from lane r of tl) and the rope parts of rows 8 w .. 8 w + 7 (k = 8).
-  // The nine instructions are spread over the matrix products of a tile, so
-  // that the address unit takes them as it frees up instead of stalling the
-  // wave.  ln is the lane id, opaque to the compiler (recomputed per tile).
-  auto dma_k = [&](int k, int32_t tl, uint32_t lb, int ln) __attribute__((always_inline)) {
-    if (k < 8) {
-      const int r = wid + MLA_WAVES * k;
-      const int32_t tok = __builtin_amdgcn_readlane(tl, r);
-      const char* src = kseq_b + static_cast<uint64_t>(tok > 0 ? tok : 0) * pitch;
-      dma16(src, (16u * ln) ^ (16u * main_swz(r)), lb + 1024u * r);
-    } else {
-      const uint32_t rr = 8 * wid + (ln >> 3);
-      const int32_t tok = __shfl(tl, rr, 64);
-      const uint32_t voff = static_cast<uint32_t>(tok > 0 ? tok : 0) * static_cast<uint32_t>(pitch) + 1024u +
-                            16u * ((ln & 7) ^ rope_swz(rr));
-      dma16(kseq_b, voff, lb + KT_MAIN + 1024u * wid);
-    }
-  };
   auto tokens_of = [&](int u) __attribute__((always_inline)) -> int32_t {
     return s_tok[(u * TILE + (lane & 31)) & (TOK_RING - 1)];
   };
-  auto issue = [&](int u, int buf) __attribute__((always_inline)) {
-    const int32_t tl = tokens_of(u);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int k = 0; k < 9; ++k) dma_k(k, tl, kb_lds + buf * KT_BYTES, ln);
+  // The gather of a tile is issued by waves 4..7 only, in the segment where
+  // they compute scores, one load between every four score products (they
+  // would otherwise stall the wave that issues them).  Wave 4 + l loads the
+  // 1 KB main parts of rows l, l + 4, ..., l + 28 (k = 0..7) and the rope parts
+  // of rows 8 l .. 8 l + 7 (k = 8).  The token ids come in two registers read
+  // from the ring a segment earlier: lane r of tl holds the token of row r,
+  // lane L of t8 that of row 8 l + L / 8.
+  const int gl = wid & 3;
+  auto gather_tokens = [&](int u, int32_t& tl, int32_t& t8) __attribute__((always_inline)) {
+    tl = tokens_of(u);
+    t8 = s_tok[(u * TILE + 8 * gl + (lane >> 3)) & (TOK_RING - 1)];
+  };
+  auto gather_k = [&](int k, int32_t tl, int32_t t8, uint32_t lb, int ln) __attribute__((always_inline)) {
+    if (k < 8) {
+      const int r = gl + 4 * k;
+      const int32_t tk = __builtin_amdgcn_readlane(tl, r);
+      const char* src = kseq_b + static_cast<uint64_t>(tk > 0 ? tk : 0) * pitch;
+      dma16(src, (16u * ln) ^ (16u * main_swz(r)), lb + 1024u * r);
+    } else {
+      const uint32_t rr = 8 * gl + (ln >> 3);
+      const uint32_t voff = static_cast<uint32_t>(t8 > 0 ? t8 : 0) * static_cast<uint32_t>(pitch) + 1024u +
+                            16u * ((ln & 7) ^ rope_swz(rr));
+      dma16(kseq_b, voff, lb + KT_MAIN + 1024u * gl);
+    }
   };
   auto live_of = [&](int u) __attribute__((always_inline)) -> uint32_t {
     return static_cast<uint32_t>(__ballot(tokens_of(u) >= 0));
   };
 
-  // K fragment of S: lane (row r32, half h) reads chunk 2 ks + h of row r32,
-  // at tile offset (cs ^ 32 (ks & 7)) + 256 (ks >> 3) (main) or
-  // (cr ^ 32 (ks - 32)) (rope); the xor terms only touch bits 5..7.  The 36
-  // products run in a fixed order: product i < 32 takes chunk pair k8 = i >> 2
-  // of 256-byte group a = i & 3 (ks = 8 a + k8), i >= 32 the rope chunk pair
-  // i - 32.
-  const uint32_t cs = r32 * 1024u + 16u * (h ^ main_swz(r32));
-  const uint32_t cr = KT_MAIN + r32 * 128u + 16u * (h ^ rope_swz(r32));
-  auto kfrag = [&](const uint8_t* kt, uint32_t xs, uint32_t xr, int i) __attribute__((always_inline)) -> u32x4_t {
-    const uint8_t* ad = i < 32 ? kt + (xs ^ (32u * (i >> 2))) + 256 * (i & 3) : kt + (xr ^ (32u * (i - 32)));
-    return *reinterpret_cast<const u32x4_t*>(ad);
-  };
-  auto qfrag = [&](int i) __attribute__((always_inline)) -> u32x4_t {
-    const int ks = i < 32 ? 8 * (i & 3) + (i >> 2) : i;
-    return ks < MLA_QR ? qf[ks < MLA_QR ? ks : 0] : s_qw[(ks - MLA_QR) * 64];
-  };
-  // V^T fragment of dim block db, key half kk: lane (group g, source slot
-  // 4 m + q) addresses key 16 kk + 4 (g >> 1) + m (then + 8), dims
-  // 32 db + 16 (g & 1) + 4 q; the transposing read hands lane j of each 16-lane
-  // group dim 32 db + 16 (g & 1) + j of those four keys.  Tile offset:
-  // (cv ^ 64 (db & 3)) + 256 (db >> 2) + 16 KB kk, the xor touching bits 6..7.
-  // PV step i (of 32): dim quarter dq = i >> 3, 256-byte group dh = (i >> 1) & 3
-  // (dim block db = 4 dh + dq), key half kk = i & 1.
-  uint32_t cv1, cv2;
-  {
-    const uint32_t g4 = lane >> 4, m4 = (lane >> 2) & 3, q4 = lane & 3;
-    const uint32_t R1 = 4 * (g4 >> 1) + m4, R2 = R1 + 8;
-    const uint32_t f1 = main_swz(R1), f2 = main_swz(R2), lo_c = 2 * (g4 & 1) + (q4 >> 1);
-    cv1 = R1 * 1024 + 64 * (f1 >> 2) + 16 * (lo_c ^ (f1 & 3)) + 8 * (q4 & 1);
-    cv2 = R2 * 1024 + 64 * (f2 >> 2) + 16 * (lo_c ^ (f2 & 3)) + 8 * (q4 & 1);
-  }
-  auto vfrag = [&](uint8_t* kt, uint32_t x1, uint32_t x2, int i) __attribute__((always_inline)) -> u32x4_t {
-    const int dq = i >> 3, off = 16384 * (i & 1) + 256 * ((i >> 1) & 3);
-    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + (x1 ^ (64u * dq)) + off));
-    const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + (x2 ^ (64u * dq)) + off));
-    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
-    return u32x4_t{a2.x, a2.y, b2.x, b2.y};
-  };
-  // dead keys of a tile (bit clear in `live`) get score -inf
-  auto mask_dead = [&](f32x16_t& sacc, uint32_t live) __attribute__((always_inline)) {
-    const uint32_t lm = live >> (4 * h);
+  // K fragment of key block mb, contraction step ks: lane (col, q) reads its
+  // chunk of tile row 16 mb + col, at (cs ^ 16 (ks & 3)) + 256 (ks >> 2)
+  // + 16 KB mb (main part, ks < 16) or (cr ^ 16 (ks - 16)) + 2 KB mb (rope);
+  // the xor terms only touch bits 4..5
+  const uint32_t cs = col * 1024u + ((64u * q) ^ (16u * main_swz(col)));
+  const uint32_t cr = KT_MAIN + col * 128u + ((32u * q) ^ (16u * rope_swz(col)));
+  constexpr int SD = 4;   // K fragments read ahead (products in the order ks, mb)
+  // scores of the tile in buffer bs, for key blocks 0 and 1
+  auto scores = [&](auto with_gather, int bs, f32x4_t& s0, f32x4_t& s1, int32_t tl, int32_t t8,
+                    int bg) __attribute__((always_inline)) {
+    uint32_t xs = cs, xr = cr;
+    int ln = lane;
+    asm volatile("" : "+v"(xs), "+v"(xr), "+v"(ln));   // a few bases per tile, not 36 live offsets
+    const uint32_t lb = kb_lds + bg * KT_BYTES;
+    const uint8_t* kt = s_kb + bs * KT_BYTES;
+    auto frag = [&](int i) __attribute__((always_inline)) -> u32x4_t {
+      const int ks = i >> 1, mb = i & 1;
+      const uint8_t* ad = ks < 16 ? kt + (xs ^ (16u * (ks & 3))) + 256 * (ks >> 2) + 16384 * mb
+                                  : kt + (xr ^ (16u * (ks - 16))) + 2048 * mb;
+      return *reinterpret_cast<const u32x4_t*>(ad);
+    };
+    u32x4_t kf[SD];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (!((lm >> (8 * (j >> 2) + (j & 3))) & 1u)) sacc[j] = NEG_INF;
+    for (int i = 0; i < SD; ++i) kf[i] = frag(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, SD, 0);   // the first SD LDS reads lead
+    s0 = f32x4_t{};
+    s1 = f32x4_t{};
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      if (i & 1) s1 = mfma16x16x32_bf16(kf[i % SD], qf[i >> 1], s1);
+      else s0 = mfma16x16x32_bf16(kf[i % SD], qf[i >> 1], s0);
+      if (i + SD < 36) kf[i % SD] = frag(i + SD);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // and one LDS read, in turn
+      if constexpr (decltype(with_gather)::value)
+        if ((i & 3) == 3) gather_k(i >> 2, tl, t8, lb, ln);
+    }
   };
-  // softmax of a tile's S^T accumulator: reg j holds key 8 (j >> 2) + 4 h + (j & 3)
-  // of head r32.  Returns the factor that rescales what was accumulated before.
-  auto softmax = [&](const f32x16_t& sacc, u32x4_t (&ph)[2], u32x4_t (&pl)[2]) __attribute__((always_inline)) -> float {
-    float sv[16];
+  // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
+  // P^T fragments (k slot j < 4: key 4 q + j; j >= 4: key 16 + 4 q + j - 4)
+  // and returns the factor that rescales what was accumulated before.
+  auto softmax = [&](f32x4_t s0, f32x4_t s1, uint32_t live, u32x4_t& ph, u32x4_t& pl) __attribute__((always_inline)) -> float {
+    if (live != 0xffffffffu) {
+      const uint32_t lm = live >> (4 * q);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
-    float tmax = sv[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sv[j]);
-    tmax = swap_halves_max(tmax);
-    // branch-free, so that it can run between the matrix products
+      for (int j = 0; j < 4; ++j) {
+        if (!((lm >> j) & 1u)) s0[j] = NEG_INF;
+        if (!((lm >> (16 + j)) & 1u)) s1[j] = NEG_INF;
+      }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    tmax = quad_max(tmax);
     const bool first = m_run == NEG_INF;
     const bool grow = !first && (tmax - m_run) * c2 > 8.f;
     const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
     const float alpha = grow ? a : 1.f;
     m_run = (first || grow) ? tmax : m_run;
     const float mb = m_run == NEG_INF ? 0.f : m_run * c2;   // an all-dead prefix gives zero weights
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -mb));
+      x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb));
+    }
+    uint32_t hv[4], lv[4];
     float psum = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint32_t hv[4], lv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * kk + 2 * i], c2, -mb));
-        const float x1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * kk + 2 * i + 1], c2, -mb));
-        hv[i] = pack_bf16x2(x0, x1);
-        lv[i] = pack_bf16x2(x0 - __uint_as_float(hv[i] << 16), x1 - __uint_as_float(hv[i] & 0xffff0000u));
-        psum += x0 + x1;
-      }
-      ph[kk] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-      pl[kk] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+    for (int i = 0; i < 4; ++i) {
+      hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
+      psum += x[2 * i] + x[2 * i + 1];
     }
-    l_run = l_run * alpha + swap_halves_sum(psum);
+    ph = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+    pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+    l_run = l_run * alpha + quad_sum(psum);
     return alpha;
   };
-  // o *= alpha (rare): element by element through one VGPR, written so that
-  // the accumulators keep living in the accumulation registers
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (alpha != 1.f) {
 #pragma unroll
-      for (int db = 0; db < 16; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x = o[db][j], tmp;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(x), "=&v"(tmp)
-                       : "v"(alpha));
-          o[db][j] = x;
-        }
+      for (int db = 0; db < 32; ++db) o[db] *= alpha;
     }
   };
-  u32x4_t ph[2] = {u32x4_t{}, u32x4_t{}}, pl[2] = {u32x4_t{}, u32x4_t{}};
-  auto pv_mfma = [&](int i, const u32x4_t& va) __attribute__((always_inline)) {
-    const int db = 4 * ((i >> 1) & 3) + (i >> 3), kk = i & 1;
-    o[db] = mfma32x32x16_bf16(va, ph[kk], o[db]);
-    o[db] = mfma32x32x16_bf16(va, pl[kk], o[db]);
-  };
-  constexpr int SD = 4;   // K fragments read ahead
-  constexpr int VD = 2;   // V^T fragments read ahead
-
-  // One tile step: PV of tile t (buffer bp) with the pending weights, S of
-  // tile t + 1 (buffer bs), its softmax, and the gather of tile t + 2 (buffer
-  // bg).  Phase 1 interleaves the 36 S products with the first 16 PV steps
-  // and the nine gather loads; phase 2 runs the softmax between the last 16
-  // PV steps.  The S products accumulate in one fixed order, so results do
-  // not depend on the schedule.
-  auto tile_step = [&](int bp, int bs, int bg, uint32_t live_n, int u_gather) __attribute__((always_inline)) {
-    uint32_t xs = cs, xr = cr, x1 = cv1, x2 = cv2;
-    int ln = lane;
-    asm volatile("" : "+v"(xs), "+v"(xr), "+v"(x1), "+v"(x2), "+v"(ln));   // recomputed per tile
-    const uint8_t* ks_t = s_kb + bs * KT_BYTES;
-    uint8_t* kp_t = s_kb + bp * KT_BYTES;
-    const int32_t tl = tokens_of(u_gather);
-    const uint32_t lb = kb_lds + bg * KT_BYTES;
-    u32x4_t kf[SD], vf[VD];
-#pragma unroll
-    for (int i = 0; i < SD; ++i) kf[i] = kfrag(ks_t, xs, xr, i);
-#pragma unroll
-    for (int i = 0; i < VD; ++i) vf[i] = vfrag(kp_t, x1, x2, i);
-    __builtin_amdgcn_sched_group_barrier(0x100, SD + 2 * VD, 0);
-    f32x16_t sacc = f32x16_t{};
-    auto s_item = [&](int si) __attribute__((always_inline)) {
-      sacc = mfma32x32x16_bf16(kf[si % SD], qfrag(si), sacc);
-      if (si + SD < 36) kf[si % SD] = kfrag(ks_t, xs, xr, si + SD);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  // V^T fragment of dim block db: lane (q, source slot 4 m + r) addresses key
+  // 4 q + m (then 16 + 4 q + m), dims 16 db + 4 r; the transposing read hands
+  // lane j of each 16-lane group dim 16 db + j of those four keys.  Tile
+  // offset: (cv ^ 32 (db & 7)) + 256 (db >> 3) (+ 16 KB for the second read),
+  // the xor touching bits 5..7.
+  uint32_t cv;
+  {
+    const uint32_t m4 = (lane >> 2) & 3, r4 = lane & 3, R = 4 * q + m4, f = main_swz(R);
+    cv = R * 1024 + 16 * ((r4 >> 1) ^ (f & 1)) + 16 * (f & 14) + 8 * (r4 & 1);
+  }
+  constexpr int VD = 3;   // V^T fragments read ahead
+  auto pv = [&](int bp, const u32x4_t& ph, const u32x4_t& pl) __attribute__((always_inline)) {
+    uint32_t x1 = cv;
+    asm volatile("" : "+v"(x1));
+    uint8_t* kt = s_kb + bp * KT_BYTES;
+    auto vfrag = [&](int db) __attribute__((always_inline)) -> u32x4_t {
+      uint8_t* ad = kt + (x1 ^ (32u * (db & 7))) + 256 * (db >> 3);
+      const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)ad);
+      const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ad + 16384));
+      const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+      return u32x4_t{a2.x, a2.y, b2.x, b2.y};
     };
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s_item(2 * i);
-      s_item(2 * i + 1);
-      pv_mfma(i, vf[i % VD]);
-      vf[i % VD] = vfrag(kp_t, x1, x2, i + VD);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if ((i & 1) && i < 16) dma_k(i >> 1, tl, lb, ln);
-    }
-#pragma unroll
-    for (int i = 32; i < 36; ++i) s_item(i);
-    dma_k(8, tl, lb, ln);
-    if (live_n != 0xffffffffu) mask_dead(sacc, live_n);
-    u32x4_t nh[2], nl[2];
-    const float alpha = softmax(sacc, nh, nl);
-#pragma unroll
-    for (int i = 16; i < 32; ++i) {
-      pv_mfma(i, vf[i % VD]);
-      if (i + VD < 32) vf[i % VD] = vfrag(kp_t, x1, x2, i + VD);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    rescale(alpha);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      ph[kk] = nh[kk];
-      pl[kk] = nl[kk];
-    }
-  };
-  // PV of the last tile
-  auto pv_last = [&](int bp) __attribute__((always_inline)) {
-    uint32_t x1 = cv1, x2 = cv2;
-    asm volatile("" : "+v"(x1), "+v"(x2));
-    uint8_t* kp_t = s_kb + bp * KT_BYTES;
     u32x4_t vf[VD];
 #pragma unroll
-    for (int i = 0; i < VD; ++i) vf[i] = vfrag(kp_t, x1, x2, i);
+    for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VD, 0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      pv_mfma(i, vf[i % VD]);
-      if (i + VD < 32) vf[i % VD] = vfrag(kp_t, x1, x2, i + VD);
+    for (int db = 0; db < 32; ++db) {
+      o[db] = mfma16x16x32_bf16(vf[db % VD], ph, o[db]);
+      o[db] = mfma16x16x32_bf16(vf[db % VD], pl, o[db]);
+      if (db + VD < 32) vf[db % VD] = vfrag(db + VD);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
-  // S and softmax of the first tile
-  auto s_first = [&](uint32_t live0) __attribute__((always_inline)) {
-    uint32_t xs = cs, xr = cr;
-    const uint8_t* ks_t = s_kb;
-    f32x16_t sacc = f32x16_t{};
-#pragma unroll
-    for (int i = 0; i < 36; ++i) sacc = mfma32x32x16_bf16(kfrag(ks_t, xs, xr, i), qfrag(i), sacc);
-    if (live0 != 0xffffffffu) mask_dead(sacc, live0);
-    softmax(sacc, ph, pl);
-  };
 
-  // token ring refill: entries of tiles t + 16 .. t + 31 are fetched at t = 16 j
-  // and validated and stored one iteration later (their loads have landed by
-  // then) into the slots of tiles t - 16 .. t - 1
-  const bool token_mode = p.idx != nullptr && p.c == 1;
-  auto ring_fetch = [&](int64_t pos) __attribute__((always_inline)) -> int32_t {
-    if (token_mode) return p.idx[row * p.k_sel + (pos < p1 ? pos : p1 - 1)];
-    return pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
-  };
-  auto ring_value = [&](int64_t pos, int32_t v) __attribute__((always_inline)) -> int32_t {
-    if (pos >= p1) return -1;
-    if (token_mode) return (v >= 0 && v < si.n_vis) ? v : -1;
-    return v;
-  };
-  int32_t ring_v[2] = {-1, -1};
+  // the first two tiles
   __syncthreads();   // token ring filled
-  if (n_tiles > 0) issue(0, 0);
-  if (n_tiles > 1) issue(1, 1);
+  int32_t g_tl = 0, g_t8 = 0;   // token ids of the next tile to gather
+  if (grp == 1) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    for (int u = 0; u < 2 && u < n_tiles; ++u) {
+      gather_tokens(u, g_tl, g_t8);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) gather_k(k, g_tl, g_t8, kb_lds + u * KT_BYTES, ln);
+    }
+    if (n_tiles > 2) gather_tokens(2, g_tl, g_t8);
+  }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
-  if (n_tiles > 0 && wvalid) s_first(live_of(0));
 
-  for (int t = 0; t + 1 < n_tiles; ++t) {
-    if (t > 0) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);   // this thread's part of tile t + 1 has landed
-      __syncthreads();                      // tile t + 1 complete; tile t - 1 released
+  // token ring refill: entries of tiles 16 j + 16 .. 16 j + 31 are fetched in
+  // segment 32 j + 1, land by the wait that closes segment 32 j + 2, and are
+  // validated and stored in segment 32 j + 3, into the slots of tiles
+  // 16 j - 16 .. 16 j - 1, which segment 32 j read last
+  const bool token_mode = p.idx != nullptr && p.c == 1;
+  int32_t ring_v = -1;
+  // the part of segment sg that every wave does: its share of the ring refill
+  auto segment_io = [&](int sg) __attribute__((always_inline)) {
+    const int m = sg >> 1;
+    if ((sg & 31) == 1 && sg > 32 && m + 16 < n_tiles) {
+      const int64_t pos = p0 + static_cast<int64_t>(m + 16) * TILE + tid;
+      if (token_mode) ring_v = p.idx[row * p.k_sel + (pos < p1 ? pos : p1 - 1)];
+      else ring_v = pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
     }
-    if ((t % TOK_REFILL) == 1 && t > TOK_REFILL && (t - 1 + TOK_REFILL) < n_tiles) {
-      const int base = (t - 1 + TOK_REFILL) * TILE;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        s_tok[(base + tid + 256 * k) & (TOK_RING - 1)] = ring_value(p0 + base + tid + 256 * k, ring_v[k]);
+    if ((sg & 31) == 3 && sg > 32 && m + 15 < n_tiles) {
+      const int base = (m + 15) * TILE;   // m + 15 = 16 j + 16
+      const int64_t pos = p0 + base + tid;
+      int32_t v = ring_v;
+      if (pos >= p1) v = -1;
+      else if (token_mode && !(v >= 0 && v < si.n_vis)) v = -1;
+      s_tok[(base + tid) & (TOK_RING - 1)] = v;
     }
-    if ((t % TOK_REFILL) == 0 && t >= TOK_REFILL && (t + TOK_REFILL) < n_tiles) {
-      const int base = (t + TOK_REFILL) * TILE;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) ring_v[k] = ring_fetch(p0 + base + tid + 256 * k);
+  };
+  auto segment_end = [&](int sg) __attribute__((always_inline)) {
+    if ((sg & 1) == 0) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): gather of tile sg / 2 + 2 has landed
+    __syncthreads();
+  };
+  // Segment sg: waves 0..3 compute the scores and softmax of tile sg / 2
+  // (even sg) or its PV products (odd sg); waves 4..7 do the same one segment
+  // later and gather tile sg / 2 + 2 in their score segments.  Waves without
+  // heads (Hq < 128) run the same products on zero queries, so that every wave
+  // takes the same straight-line path.
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (grp == 0) {
+    for (int u = 0; u < n_tiles; ++u) {
+      segment_io(2 * u);
+      f32x4_t s0, s1;
+      u32x4_t ph, pl;
+      scores(no{}, u % KT_NBUF, s0, s1, 0, 0, 0);
+      rescale(softmax(s0, s1, live_of(u), ph, pl));
+      segment_end(2 * u);
+      segment_io(2 * u + 1);
+      pv(u % KT_NBUF, ph, pl);
+      segment_end(2 * u + 1);
     }
-    // the gather of tile t + 2 also runs past the end: it then reloads rows
-    // (of token 0) into the buffer of tile t - 1, which nothing reads again
-    const int bg = (t + 2) % KT_NBUF;
-    if (wvalid) {
-      tile_step(t % KT_NBUF, (t + 1) % KT_NBUF, bg, live_of(t + 1), t + 2);
-    } else {
-      issue(t + 2, bg);
+    segment_io(2 * n_tiles);
+    segment_end(2 * n_tiles);
+  } else {
+    segment_io(0);
+    segment_end(0);
+    for (int u = 0; u < n_tiles; ++u) {
+      // the gather of tile u + 2 also runs past the end: it then reloads rows
+      // (ring entries past the stream: token 0 or stale valid ids) into the
+      // buffer of tile u - 1, which nothing reads again
+      segment_io(2 * u + 1);
+      f32x4_t s0, s1;
+      u32x4_t ph, pl;
+      scores(yes{}, u % KT_NBUF, s0, s1, g_tl, g_t8, (u + 2) % KT_NBUF);
+      rescale(softmax(s0, s1, live_of(u), ph, pl));
+      segment_end(2 * u + 1);
+      segment_io(2 * u + 2);
+      gather_tokens(u + 3, g_tl, g_t8);   // for the next score segment
+      pv(u % KT_NBUF, ph, pl);
+      segment_end(2 * u + 2);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // no gather left in flight
-  if (n_tiles > 0 && wvalid) pv_last((n_tiles - 1) % KT_NBUF);
-  if (!hvalid) return;
+  if (!(wvalid && head < p.Hq)) return;
 
-  // accumulator (db, j) holds dim 32 db + 8 (j >> 2) + 4 h + (j & 3) of head `head`
+  // accumulator (db, j) holds dim 16 db + 4 q + j of head `head`
   if (p.n_split == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * h;
+    const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * q;
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        store4(p.out, p.o_dtype, ob + 32 * db + 8 * a, o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
-               o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+    for (int db = 0; db < 32; ++db)
+      store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
   } else {
     float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * (MLA_DV + 2);
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * a + 4 * h) =
-            f32x4_t{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
-    if (h == 0) {
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
+    if (q == 0) {
       pp[MLA_DV] = m_run;
       pp[MLA_DV + 1] = l_run;
     }
