@@ -87,6 +87,98 @@ __device__ __forceinline__ void fwht64(float (&x)[64]) {
   }
 }
 
+// Query operands of one row for the MFMA kernels: qa[rb][ks][*] is the A
+// operand of contraction step ks for heads 32 rb .. 32 rb + 31 (lane n: head
+// 32 rb + n, lane half h2: dims 64 h2 + 8 ks .. + 7), after the optional
+// rotation and the f16 prescale or bf16 split; wv[rb][j] is the head weight
+// (times the undoing scale) of accumulator row j of block rb held by the lane.
+template <int KK, int QK, int RB, int NQ>
+__device__ __forceinline__ void query_operands(const ScoreParams& p, int64_t row, int n, int h2,
+                                               u32x4_t (&qa)[RB][8][NQ], float (&wv)[RB][16]) {
+  constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
+  float fw[RB];
+  const int Hh = p.H;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int head = rb * 32 + n;
+    float x[64];
+    if (head < Hh) {
+      const int64_t base = (row * Hh + head) * 128 + 64 * h2;
+      if constexpr (QK == 0 || QK == 1) {
+        const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.q) + base);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4_t v = qp[i];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint16_t lo16 = w4[j] & 0xffffu, hi16 = w4[j] >> 16;
+            x[8 * i + 2 * j] = QK == 0 ? bf16_to_f32(lo16) : f16_to_f32(lo16);
+            x[8 * i + 2 * j + 1] = QK == 0 ? bf16_to_f32(hi16) : f16_to_f32(hi16);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = 0.f;
+    }
+    if (p.hadamard) {
+      fwht64(x);
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float o = __shfl_xor(x[i], 32, 64);
+        x[i] = (h2 == 0 ? x[i] + o : o - x[i]) * 0.088388347648318440550f;   // 1/sqrt(128)
+      }
+    }
+    float factor = 1.f;
+    if constexpr (F16OP) {
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      int e = 0;
+      if (amax > 0.f) {
+        int E;
+        frexpf(amax, &E);
+        e = 14 - E;   // amax * 2^e < 2^14: inside the f16 range with headroom
+      }
+      factor = ldexpf(1.f, -e);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint32_t wv4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wv4[j] = pack_f16x2(ldexpf(x[8 * ks + 2 * j], e), ldexpf(x[8 * ks + 2 * j + 1], e));
+        qa[rb][ks][0] = u32x4_t{wv4[0], wv4[1], wv4[2], wv4[3]};
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint32_t hv[4], lv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = x[8 * ks + 2 * j], b = x[8 * ks + 2 * j + 1];
+          const float ah = bf16_to_f32(f32_to_bf16(a)), bh = bf16_to_f32(f32_to_bf16(b));
+          hv[j] = pack_bf16x2(ah, bh);
+          lv[j] = pack_bf16x2(a - ah, b - bh);
+        }
+        qa[rb][ks][0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+        if constexpr (NQ == 2) qa[rb][ks][NQ - 1] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+      }
+    }
+    float wh = head < Hh ? p.w[row * Hh + head] : 0.f;
+    if constexpr (KK == KK_FP8) factor *= 256.f;   // undo the 2^-8 of the fp8 -> f16 map
+    fw[rb] = wh * factor;
+  }
+
+  // head weight of each accumulator row held by this lane
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wv[rb][j] = __shfl(fw[rb], 8 * (j >> 2) + 4 * h2 + (j & 3), 64);
+
+}
+
 template <int KK, int QK, int RB, int NQ>
 __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
   constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
@@ -128,89 +220,9 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
   const int64_t nf = (p.c == 1 && p.n_sink < n_vis) ? p.n_sink : (p.c == 1 ? n_vis : 0);
 
   if (active && c_end > u_begin) {
-    // ---------------------------------------------------- query operand --
-    const int Hh = p.H;
     u32x4_t qa[RB][8][NQ];
-    float fw[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int head = rb * 32 + n;
-      float x[64];
-      if (head < Hh) {
-        const int64_t base = (row * Hh + head) * 128 + 64 * h2;
-        if constexpr (QK == 0 || QK == 1) {
-          const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.q) + base);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const u32x4_t v = qp[i];
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint16_t lo16 = w4[j] & 0xffffu, hi16 = w4[j] >> 16;
-              x[8 * i + 2 * j] = QK == 0 ? bf16_to_f32(lo16) : f16_to_f32(lo16);
-              x[8 * i + 2 * j + 1] = QK == 0 ? bf16_to_f32(hi16) : f16_to_f32(hi16);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 64; ++i) x[i] = 0.f;
-      }
-      if (p.hadamard) {
-        fwht64(x);
-#pragma unroll
-        for (int i = 0; i < 64; ++i) {
-          const float o = __shfl_xor(x[i], 32, 64);
-          x[i] = (h2 == 0 ? x[i] + o : o - x[i]) * 0.088388347648318440550f;   // 1/sqrt(128)
-        }
-      }
-      float factor = 1.f;
-      if constexpr (F16OP) {
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        int e = 0;
-        if (amax > 0.f) {
-          int E;
-          frexpf(amax, &E);
-          e = 14 - E;   // amax * 2^e < 2^14: inside the f16 range with headroom
-        }
-        factor = ldexpf(1.f, -e);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          uint32_t wv4[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            wv4[j] = pack_f16x2(ldexpf(x[8 * ks + 2 * j], e), ldexpf(x[8 * ks + 2 * j + 1], e));
-          qa[rb][ks][0] = u32x4_t{wv4[0], wv4[1], wv4[2], wv4[3]};
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          uint32_t hv[4], lv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float a = x[8 * ks + 2 * j], b = x[8 * ks + 2 * j + 1];
-            const float ah = bf16_to_f32(f32_to_bf16(a)), bh = bf16_to_f32(f32_to_bf16(b));
-            hv[j] = pack_bf16x2(ah, bh);
-            lv[j] = pack_bf16x2(a - ah, b - bh);
-          }
-          qa[rb][ks][0] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-          if constexpr (NQ == 2) qa[rb][ks][NQ - 1] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
-        }
-      }
-      float wh = head < Hh ? p.w[row * Hh + head] : 0.f;
-      if constexpr (KK == KK_FP8) factor *= 256.f;   // undo the 2^-8 of the fp8 -> f16 map
-      fw[rb] = wh * factor;
-    }
-
-    // head weight of each accumulator row held by this lane
     float wv[RB][16];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) wv[rb][j] = __shfl(fw[rb], 8 * (j >> 2) + 4 * h2 + (j & 3), 64);
+    query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
 
     // -------------------------------------------------------- key stream --
     const int64_t key_row0 = static_cast<int64_t>(s) * p.n_units;
@@ -278,6 +290,142 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
   }
 }
 
+// Prefill variant (n_q a multiple of 4, no histogram): one workgroup = 4
+// consecutive query rows of one sequence (one wave each) x one chunk of
+// 32-key tiles, taken two tiles at a time.  The key tiles are gathered once
+// per workgroup into LDS with direct global -> LDS loads, one tile pair
+// ahead, and read by all four waves; the products of the second tile of a
+// pair are issued before the epilogue of the first.  The scores of the chunk
+// collect in LDS and leave in one coalesced pass at the end (so that no store
+// sits between the tile loads in the memory queue).  Tile layout: key row r
+// (256 bytes, 2-byte keys, D = 128) keeps its 16-byte chunk c in slot
+// c ^ (r & 15), so that a wave's B-operand read (lane n: row n, chunk
+// 8 h2 + ks) is free of LDS bank conflicts.
+constexpr int SC_PAIR_BYTES = 2 * 32 * 256;   // two key tiles
+constexpr int SC_NBUF = 3;                      // tile pairs: computing, landed, in flight
+constexpr int SC_MAX_TILES = 32;                // chunk_tiles bound for this kernel
+constexpr size_t SC_LDS = SC_NBUF * SC_PAIR_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
+
+typedef __attribute__((address_space(3))) void sc_lds_void_t;
+
+__device__ __forceinline__ void sc_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int KK, int QK, int RB, int NQ>
+__global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
+  static_assert(KK == KK_BF16 || KK == KK_F16, "2-byte keys only");
+  constexpr bool F16OP = KK == KK_F16;
+  extern __shared__ __align__(16) uint8_t s_raw[];
+  uint8_t* s_kt = s_raw;                                                      // SC_NBUF tile pairs
+  float* s_sc = reinterpret_cast<float*>(s_raw + SC_NBUF * SC_PAIR_BYTES);   // [4][chunk_tiles * 32]
+  int32_t* s_tend = reinterpret_cast<int32_t*>(s_sc + 4 * SC_MAX_TILES * 32);
+
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 31, h2 = lane >> 5;
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const int64_t nrg = rows >> 2;
+  const int64_t row = (nrg - 1 - static_cast<int64_t>(blockIdx.x) / p.n_chunks) * 4 + wid;
+  const int chunk = blockIdx.x % p.n_chunks;
+  const int s = static_cast<int>(row / p.n_q);   // the same for the 4 rows (n_q % 4 == 0)
+  const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
+  const int64_t n_vis = visible_tokens(p.q_pos[row], kl, p.n_units * p.c) / p.c;
+  const int64_t u_begin = static_cast<int64_t>(chunk) * p.chunk_tiles * 32;
+  int64_t u_end = u_begin + static_cast<int64_t>(p.chunk_tiles) * 32;
+  if (u_end > p.n_units) u_end = p.n_units;
+  const int64_t c_end = n_vis < u_end ? n_vis : u_end;   // this row computes [u_begin, c_end)
+  const int t_own = c_end > u_begin ? static_cast<int>((c_end - u_begin + 31) >> 5) : 0;
+  if (lane == 0) s_tend[wid] = t_own;
+  __syncthreads();
+  const int n_t = max(max(s_tend[0], s_tend[1]), max(s_tend[2], s_tend[3]));   // tiles of the workgroup
+  const int n_pairs = (n_t + 1) >> 1;
+
+  // gather of tile pair T into slot T % SC_NBUF: wave w loads rows 8 w .. 8 w + 7
+  // of both tiles (four 1 KB loads; lane L of load i: tile i >> 1, row
+  // 8 w + 4 (i & 1) + L / 16, slot L & 15)
+  const uint32_t kt_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((sc_lds_void_t*)s_kt));
+  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * 256;
+  auto issue = [&](int T) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * wid + 4 * (i & 1) + (ln >> 4);
+      int64_t u = u_begin + static_cast<int64_t>(2 * T + (i >> 1)) * 32 + r;
+      if (u >= p.n_units) u = p.n_units - 1;   // past the end: any valid row, never used
+      const uint32_t voff = static_cast<uint32_t>(u) * 256u + 16u * ((ln & 15) ^ (r & 15));
+      sc_dma16(kbase, voff,
+               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_PAIR_BYTES + 8192u * (i >> 1) +
+                                              1024u * (2 * wid + (i & 1))));
+    }
+  };
+  if (n_pairs > 0) issue(0);
+  if (n_pairs > 1) issue(1);
+
+  u32x4_t qa[RB][8][NQ];
+  float wv[RB][16];
+  query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
+  const uint32_t b_off = n * 256u;   // + 16 ((8 h2 + ks) ^ (n & 15))
+
+  auto products = [&](const uint8_t* kt, uint32_t hx, f32x16_t (&acc)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(kt + 16u * ((hx + ks) ^ (n & 15)));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (F16OP) {
+          acc[rb] = mfma32x32x16_f16(qa[rb][ks][0], bh, acc[rb]);
+        } else {
+          acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bh, acc[rb]);
+          if constexpr (NQ == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][NQ - 1], bh, acc[rb]);
+        }
+      }
+    }
+  };
+  // ReLU, head weight and head sum (four partial sums, then the lane halves)
+  auto epilogue = [&](const f32x16_t (&acc)[RB], int t) __attribute__((always_inline)) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part[j & 3] = fmaf(wv[rb][j], fmaxf(acc[rb][j], 0.f), part[j & 3]);
+    const float sum = (part[0] + part[1]) + (part[2] + part[3]);
+    const float tot = sum + __shfl_xor(sum, 32, 64);
+    const int64_t u = u_begin + static_cast<int64_t>(t) * 32 + n;
+    if (h2 == 0) s_sc[wid * (SC_MAX_TILES * 32) + t * 32 + n] = u < n_vis ? tot : NEG_INF;
+  };
+
+  for (int T = 0; T < n_pairs; ++T) {
+    // pair T has landed: only the four loads of pair T + 1 may still be in flight
+    if (T + 1 < n_pairs) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
+    __syncthreads();                                             // for every wave; slot of T - 1 free
+    if (T + 2 < n_pairs) issue(T + 2);
+    if (2 * T < t_own) {
+      const uint8_t* kt = s_kt + (T % SC_NBUF) * SC_PAIR_BYTES + b_off;
+      uint32_t hx = 8u * h2;
+      asm volatile("" : "+v"(hx));
+      f32x16_t acc0[RB], acc1[RB];
+      products(kt, hx, acc0);
+      products(kt + 8192, hx, acc1);   // the second tile (past t_own: computed, not kept)
+      epilogue(acc0, 2 * T);
+      epilogue(acc1, 2 * T + 1);
+    }
+  }
+  // write-out: computed tiles, then -inf for the invisible rest when asked
+  __syncthreads();
+  const int64_t w_end = p.fill_invisible ? u_end : u_begin + static_cast<int64_t>(t_own) * 32 < u_end
+                                                       ? u_begin + static_cast<int64_t>(t_own) * 32 : u_end;
+  float* orow = p.scores + row * p.n_units;
+  for (int64_t u = u_begin + lane; u < w_end; u += 64) {
+    const int i = static_cast<int>(u - u_begin);
+    orow[u] = i < t_own * 32 ? s_sc[wid * (SC_MAX_TILES * 32) + i] : NEG_INF;
+  }
+}
+
 // Generic path: any element types, H <= 128, D <= 256.  One thread per
 // (row, unit); the row's (rotated) query and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
@@ -337,6 +485,23 @@ static hipError_t launch_mfma_rb(const ScoreParams& p, dim3 grid, size_t lds, hi
   return hipGetLastError();
 }
 
+// the tiled prefill kernel covers 2-byte keys, n_q a multiple of 4, no histogram
+static bool scores_use_tiled(const ScoreParams& p) {
+  return (p.k_dtype == DSA_BF16 || p.k_dtype == DSA_F16) && p.n_q % 4 == 0 && p.hist == nullptr &&
+         p.chunk_tiles <= SC_MAX_TILES && p.n_units < (int64_t(1) << 24);   // 32-bit row offsets
+}
+
+template <int KK, int QK, int NQ>
+static hipError_t launch_tiled_rb(const ScoreParams& p, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const dim3 grid(static_cast<unsigned>((rows / 4) * p.n_chunks));
+  if (p.H <= 32)
+    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 1, NQ>), grid, dim3(256), SC_LDS, st, p);
+  else
+    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 2, NQ>), grid, dim3(256), SC_LDS, st, p);
+  return hipGetLastError();
+}
+
 // q enters the MFMA as one f16 operand (f16/fp8 keys, after a power-of-two
 // prescale) or as bf16; a bf16 q that is not rotated is exact in one bf16
 // operand, anything else is split into a bf16 high part and a bf16 residual.
@@ -344,6 +509,13 @@ template <int KK>
 static hipError_t launch_mfma_q(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t st) {
   constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
   const bool split = !F16OP && (p.q_dtype != DSA_BF16 || p.hadamard);
+  if constexpr (KK == KK_BF16 || KK == KK_F16) {
+    if (scores_use_tiled(p)) {
+      if (p.q_dtype == DSA_BF16)
+        return split ? launch_tiled_rb<KK, 0, 2>(p, st) : launch_tiled_rb<KK, 0, 1>(p, st);
+      return split ? launch_tiled_rb<KK, 1, 2>(p, st) : launch_tiled_rb<KK, 1, 1>(p, st);
+    }
+  }
   if (p.q_dtype == DSA_BF16)
     return split ? launch_mfma_rb<KK, 0, 2>(p, grid, lds, st) : launch_mfma_rb<KK, 0, 1>(p, grid, lds, st);
   return split ? launch_mfma_rb<KK, 1, 2>(p, grid, lds, st) : launch_mfma_rb<KK, 1, 1>(p, grid, lds, st);
