@@ -92,6 +92,18 @@ __device__ __forceinline__ void fwht64(float (&x)[64]) {
 // 32 rb + n, lane half h2: dims 64 h2 + 8 ks .. + 7), after the optional
 // rotation and the f16 prescale or bf16 split; wv[rb][j] is the head weight
 // (times the undoing scale) of accumulator row j of block rb held by the lane.
+// max(x, 0) as one integer max on the bit pattern: a float with the sign bit
+// set is a negative integer, and a non-negative float orders as its integer
+// (fmaxf would first quiet a NaN input with a second max instruction)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// the sum of x over the two 32-lane halves of the wave, in the same order in
+// every lane
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int KK, int QK, int RB, int NQ>
 __device__ __forceinline__ void query_operands(const ScoreParams& p, int64_t row, int n, int h2,
                                                u32x4_t (&qa)[RB][8][NQ], float (&wv)[RB][16]) {
@@ -101,6 +113,14 @@ __device__ __forceinline__ void query_operands(const ScoreParams& p, int64_t row
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int head = rb * 32 + n;
+    if constexpr (QK == 0 && !F16OP && NQ == 1) {   // bf16 q, used as it is
+      const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.q) +
+                                                           (row * Hh + (head < Hh ? head : 0)) * 128 + 64 * h2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qa[rb][ks][0] = head < Hh ? qp[ks] : u32x4_t{0u, 0u, 0u, 0u};
+      fw[rb] = head < Hh ? p.w[row * Hh + head] : 0.f;
+      continue;
+    }
     float x[64];
     if (head < Hh) {
       const int64_t base = (row * Hh + head) * 128 + 64 * h2;
@@ -257,12 +277,12 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
         }
       }
       // epilogue: ReLU, head weight, head sum
-      float part = 0.f;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) part = fmaf(wv[rb][j], fmaxf(acc[rb][j], 0.f), part);
-      float tot = part + __shfl_xor(part, 32, 64);
+        for (int j = 0; j < 16; ++j) part[j & 3] = fmaf(wv[rb][j], relu(acc[rb][j]), part[j & 3]);
+      float tot = half_sum((part[0] + part[1]) + (part[2] + part[3]));
       const int64_t u = static_cast<int64_t>(t) * 32 + n;
       if constexpr (KK == KK_FP8) {
         if (u < p.n_units) tot *= p.k_scale[key_row0 + u];
@@ -325,9 +345,21 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 31, h2 = lane >> 5;
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  // Workgroups go to the 8 XCDs in turn (block b to XCD b % 8), and inside an
+  // XCD to its 4 shader engines in turn.  XCD x takes row groups x, x + 8,
+  // x + 16, ... (the longest rows first), each with all of its chunks back to
+  // back, so that the causal work is spread evenly over the XCDs and the
+  // chunks of a row group find its q in the same L2; the chunk order turns
+  // by one from one row group to the next, so that no shader engine always
+  // draws the same chunk (the causal mask makes the late chunks the short
+  // ones).
   const int64_t nrg = rows >> 2;
-  const int64_t row = (nrg - 1 - static_cast<int64_t>(blockIdx.x) / p.n_chunks) * 4 + wid;
-  const int chunk = blockIdx.x % p.n_chunks;
+  const int64_t jx = static_cast<int64_t>(blockIdx.x >> 3);
+  const int64_t gl = jx / p.n_chunks;
+  const int64_t g = gl * 8 + (blockIdx.x & 7);
+  if (g >= nrg) return;   // the padding of the last round (whole workgroup)
+  const int64_t row = (nrg - 1 - g) * 4 + wid;
+  const int chunk = static_cast<int>((jx % p.n_chunks + gl) % p.n_chunks);
   const int s = static_cast<int>(row / p.n_q);   // the same for the 4 rows (n_q % 4 == 0)
   const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
   const int64_t n_vis = visible_tokens(p.q_pos[row], kl, p.n_units * p.c) / p.c;
@@ -365,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
 
   u32x4_t qa[RB][8][NQ];
   float wv[RB][16];
-  query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
+  if (n_t > 0) query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
   const uint32_t b_off = n * 256u;   // + 16 ((8 h2 + ks) ^ (n & 15))
 
   auto products = [&](const uint8_t* kt, uint32_t hx, f32x16_t (&acc)[RB]) __attribute__((always_inline)) {
@@ -391,9 +423,8 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) part[j & 3] = fmaf(wv[rb][j], fmaxf(acc[rb][j], 0.f), part[j & 3]);
-    const float sum = (part[0] + part[1]) + (part[2] + part[3]);
-    const float tot = sum + __shfl_xor(sum, 32, 64);
+      for (int j = 0; j < 16; ++j) part[j & 3] = fmaf(wv[rb][j], relu(acc[rb][j]), part[j & 3]);
+    const float tot = half_sum((part[0] + part[1]) + (part[2] + part[3]));
     const int64_t u = u_begin + static_cast<int64_t>(t) * 32 + n;
     if (h2 == 0) s_sc[wid * (SC_MAX_TILES * 32) + t * 32 + n] = u < n_vis ? tot : NEG_INF;
   };
@@ -494,7 +525,7 @@ static bool scores_use_tiled(const ScoreParams& p) {
 template <int KK, int QK, int NQ>
 static hipError_t launch_tiled_rb(const ScoreParams& p, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
-  const dim3 grid(static_cast<unsigned>((rows / 4) * p.n_chunks));
+  const dim3 grid(static_cast<unsigned>((rows / 4 + 7) / 8 * 8 * p.n_chunks));
   if (p.H <= 32)
     hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 1, NQ>), grid, dim3(256), SC_LDS, st, p);
   else

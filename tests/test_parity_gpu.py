@@ -98,6 +98,9 @@ SCORE_CASES = {
     "ragged_40_heads_f16_q": lambda: inputs.Workload(
         "ragged", 2, 37, 1001, 980, 40, 128, torch.float16, torch.bfloat16, "normal", 0.2, 128, 1, 0,
         False, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=77),
+    "ragged_40_heads_f16_q_rows_of_4": lambda: inputs.Workload(
+        "ragged4", 2, 36, 1001, 980, 40, 128, torch.float16, torch.bfloat16, "normal", 0.2, 128, 1, 0,
+        False, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=80),
     "bf16_keys_hadamard_split_q": lambda: inputs.Workload(
         "had_bf16", 1, 20, 700, 690, 64, 128, torch.bfloat16, torch.bfloat16, "normal", 0.125, 64, 1, 0,
         True, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=78),
@@ -111,7 +114,7 @@ SCORE_CASES = {
 def test_index_scores_match_oracle(case):
     wl = SCORE_CASES[case]()
     x = inputs.generate(wl)
-    if case == "ragged_40_heads_f16_q":   # shorter caches and invisible queries
+    if case.startswith("ragged_40_heads"):   # shorter caches and invisible queries
         x["kv_len"] = torch.tensor([1001, 640], dtype=torch.int32)
         x["q_pos"][0, 0] = -1
     d = dev(x)
