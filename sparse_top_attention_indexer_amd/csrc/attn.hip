@@ -196,28 +196,6 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   const int64_t row = rows - 1 - blockIdx.x / p.n_split;     // latest (longest causal) rows first
   const int sp = blockIdx.x % p.n_split;
   const int s = static_cast<int>(row / p.n_q);
-  const StreamInfo si = stream_setup<MLA_WAVES>(p, row, s_blk, s_scr);
-  int64_t p0, p1;
-  split_range(p, sp, si.len, &p0, &p1);
-  // token mode: trailing dead entries (the -1 padding of short selections)
-  // are cut off; they would add nothing
-  if (p.idx != nullptr && p.c == 1 && p1 > p0) {
-    if (tid == 0) s_scr[8] = 0u;
-    __syncthreads();
-    const int32_t* ir = p.idx + row * p.k_sel;
-    uint32_t last = 0;   // 1 + offset of the last live entry
-    for (int64_t e = p0 + tid; e < p1; e += 64 * MLA_WAVES) {
-      const int32_t v = ir[e];
-      if (v >= 0 && v < si.n_vis) last = static_cast<uint32_t>(e - p0 + 1);
-    }
-    if (last) atomicMax(&s_scr[8], last);
-    __syncthreads();
-    p1 = p0 + s_scr[8];
-  }
-  const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
-  for (int i = tid; i < TOK_RING; i += 64 * MLA_WAVES)
-    s_tok[i] = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
-
   const int grp = wid >> 2;
   const int col = lane & 15, q = lane >> 4;
   const int head0 = blockIdx.y * 128 + wid * 16;
@@ -228,7 +206,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
   // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
   // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
-  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk.
+  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk; loaded
+  // first, so that they are in flight during the stream set-up.
   u32x4_t qf[18];
   {
     const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
@@ -238,6 +217,39 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       qf[ks] = wvalid ? *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+
+  const StreamInfo si = stream_setup<MLA_WAVES>(p, row, s_blk, s_scr);
+  int64_t p0, p1;
+  split_range(p, sp, si.len, &p0, &p1);
+  // The token ring takes the first TOK_RING stream entries.  In token mode
+  // the trailing dead entries (the -1 padding of short selections) are cut
+  // off in the same pass over the index row; they would add nothing.
+  uint32_t last = 0;   // 1 + offset of the last live entry
+  for (int i = tid; i < TOK_RING; i += 64 * MLA_WAVES) {
+    const int32_t t = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
+    s_tok[i] = t;
+    if (t >= 0) last = static_cast<uint32_t>(i + 1);
+  }
+  const bool trim = p.idx != nullptr && p.c == 1 && p1 > p0;
+  if (trim) {
+    const int32_t* ir = p.idx + row * p.k_sel;
+    for (int64_t e = p0 + TOK_RING + tid; e < p1; e += 64 * MLA_WAVES) {
+      const int32_t v = ir[e];
+      if (v >= 0 && v < si.n_vis) last = static_cast<uint32_t>(e - p0 + 1);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) last = max(last, static_cast<uint32_t>(__shfl_xor(static_cast<int>(last), o, 64)));
+    if (lane == 0) s_scr[8 + wid] = last;
+  }
+  __syncthreads();   // the ring and the per-wave ends
+  if (trim) {
+    uint32_t e = 0;
+#pragma unroll
+    for (int w = 0; w < MLA_WAVES; ++w) e = max(e, s_scr[8 + w]);
+    p1 = p0 + e;
+  }
+  const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
+
   f32x4_t o[32];
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = f32x4_t{};
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
     for (int db = 0; db < 32; ++db)
       store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
   } else {
-    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * (MLA_DV + 2);
+    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(MLA_DV);
 #pragma unroll
     for (int db = 0; db < 32; ++db)
       *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
@@ -646,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
       store4(p.out, p.o_dtype, ob + 16 * db + 4 * quad, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
              o[db][3] * inv);
   } else {
-    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * (GQA_D + 2);
+    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(GQA_D);
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -760,7 +772,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
       else static_cast<uint16_t*>(p.out)[off] = f32_to_bf16(acc[i] * inv);
     }
   } else {
-    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + h) * (p.Dv + 2);
+    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + h) * part_width(p.Dv);
     for (int i = 0; i < 4; ++i)
       if (lane + 64 * i < p.Dv) pp[lane + 64 * i] = acc[i];
     if (lane == 0) {
@@ -772,33 +784,56 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 
 // ========================================================= split combine ==
 
-// One workgroup per (row, head): merges the partials of the splits in order.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams p) {
-  const int64_t rh = blockIdx.x;
+// One wave per (row, head, 64 float4 columns of the record), four waves per
+// workgroup: merges the partials of the splits in split order.  Lane L owns
+// float4 column 64 c + L (Dv rounded up to 4; the padded tail of the last
+// column is read, never written).  The running maxima are reduced across the
+// lanes first; the split loop then keeps several splits' loads in flight.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int nv = (p.Dv + 3) >> 2;   // float4 columns
+  const int ncb = (nv + 63) >> 6;   // column blocks of 64
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  if (wv >= rows * p.Hq * ncb) return;
+  const int64_t rh = wv / ncb;
+  const int v = static_cast<int>(wv % ncb) * 64 + lane;
   const int64_t row = rh / p.Hq;
   const int h = static_cast<int>(rh % p.Hq);
-  const int W = p.Dv + 2;
+  const int W = part_width(p.Dv);
   const float* base = p.part + (row * p.n_split * p.Hq + h) * static_cast<int64_t>(W);
   const int64_t sstride = static_cast<int64_t>(p.Hq) * W;
   float M = NEG_INF;
-  for (int c = 0; c < p.n_split; ++c) M = fmaxf(M, base[c * sstride + p.Dv]);
+  for (int c = lane; c < p.n_split; c += 64) M = fmaxf(M, base[c * sstride + p.Dv]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (M != NEG_INF)
+  if (M != NEG_INF) {
+    const int vc = v < nv ? v : nv - 1;   // lanes past the record read a valid column, write nothing
+#pragma unroll 8
     for (int c = 0; c < p.n_split; ++c) {
-      const float mc = base[c * sstride + p.Dv];
-      if (mc != NEG_INF) L += exp2f((mc - M) * p.scale_log2) * base[c * sstride + p.Dv + 1];
+      const float* rec = base + c * sstride;
+      const float mc = rec[p.Dv];
+      const float wc = mc != NEG_INF ? exp2f((mc - M) * p.scale_log2) : 0.f;
+      L += wc * rec[p.Dv + 1];
+      const f32x4_t o = *reinterpret_cast<const f32x4_t*>(rec + 4 * vc);
+      acc[0] += wc * o[0];
+      acc[1] += wc * o[1];
+      acc[2] += wc * o[2];
+      acc[3] += wc * o[3];
     }
+  }
+  if (v >= nv) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = threadIdx.x; d < p.Dv; d += blockDim.x) {
-    float acc = 0.f;
-    if (M != NEG_INF)
-      for (int c = 0; c < p.n_split; ++c) {
-        const float mc = base[c * sstride + p.Dv];
-        if (mc != NEG_INF) acc += exp2f((mc - M) * p.scale_log2) * base[c * sstride + d];
-      }
-    const int64_t off = (row * p.Hq + h) * p.Dv + d;
-    if (p.o_dtype == DSA_F32) static_cast<float*>(p.out)[off] = acc * inv;
-    else static_cast<uint16_t*>(p.out)[off] = f32_to_bf16(acc * inv);
+  const int64_t off = (row * p.Hq + h) * p.Dv + 4 * v;
+  if (p.Dv % 4 == 0) {
+    store4(p.out, p.o_dtype, off, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  } else {
+    for (int j = 0; j < 4 && 4 * v + j < p.Dv; ++j) {
+      if (p.o_dtype == DSA_F32) static_cast<float*>(p.out)[off + j] = acc[j] * inv;
+      else static_cast<uint16_t*>(p.out)[off + j] = f32_to_bf16(acc[j] * inv);
+    }
   }
 }
 
@@ -810,7 +845,7 @@ void attn_plan(AttnParams& p, int64_t list_len) {
   int64_t target;
   if (p.family == ATTN_MLA) {
     wgs = rows * ((p.Hq + 127) / 128);
-    target = 512;
+    target = 128;   // the f32 partials of a split weigh as much as its gathered rows: few, long splits
   } else if (p.family == ATTN_GQA) {
     wgs = rows * ((p.Hkv + 3) / 4);
     target = 1024;
@@ -837,7 +872,7 @@ void attn_plan(AttnParams& p, int64_t list_len) {
 
 size_t attn_workspace_bytes(const AttnParams& p) {
   if (p.n_split <= 1) return 0;
-  return static_cast<size_t>(p.S) * p.n_q * p.n_split * p.Hq * (p.Dv + 2) * sizeof(float);
+  return static_cast<size_t>(p.S) * p.n_q * p.n_split * p.Hq * part_width(p.Dv) * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t before_combine) {
@@ -870,7 +905,8 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (before_combine && (e = hipEventRecord(before_combine, st)) != hipSuccess) return e;
   if (p.n_split > 1) {
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(rows * p.Hq)), dim3(128), 0, st, p);
+    const int64_t waves = rows * p.Hq * ((p.Dv + 255) / 256);   // (row, head, 64 float4 columns)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st, p);
     e = hipGetLastError();
   }
   return e;

@@ -77,6 +77,11 @@ hipError_t launch_block_pool(const void* k_raw, int dtype, int S, int64_t n_kv, 
                              float* pooled, hipStream_t st);
 
 // --------------------------------------------------------------- attention --
+// floats per split partial record of one (row, split, head): the Dv
+// unnormalised output sums, the running max m and the sum l, padded to a
+// multiple of 4 floats so that every record starts 16-byte aligned
+constexpr int part_width(int dv) { return (dv + 2 + 3) & ~3; }
+
 struct AttnParams {
   const void* q;
   const void* k;
@@ -87,7 +92,7 @@ struct AttnParams {
   const int32_t* kv_len;
   const int32_t* idx;    // null = dense
   void* out;
-  float* part;           // split partials [rows][n_split][Hq][Dv + 2]
+  float* part;           // split partials [rows][n_split][Hq][part_width(Dv)]: o, then m and l
   int32_t dtype, o_dtype;
   int32_t S, n_q, Hq, Hkv, Dk, Dv;
   int64_t n_kv;
