@@ -17,6 +17,8 @@
 //   key: each lane streams 64 contiguous dims, and the same permutation is
 //   applied to q.  The head sum is an in-lane sum of 16 accumulators per row
 //   block plus one exchange between lane halves.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 #include "../../include/dsa.h"
@@ -457,6 +459,216 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
   }
 }
 
+// Decode variant (rows with the fused top-k histogram, 1- or 2-byte keys):
+// one wave per (query row, chunk of 32-key tiles), four chunks of one row per
+// workgroup, one wave per SIMD.  Each wave streams its own key tiles with
+// coalesced loads (every load instruction moves 1 KB of contiguous key rows;
+// a lane-per-key load would touch 64 cache lines per instruction for 16
+// bytes each) through a ring of four tiles in registers (four tiles in flight
+// per wave keep enough bytes moving to cover the loaded memory latency), and
+// writes each tile into one of two LDS buffers from which the B operands are
+// read in the MFMA layout.  Row r of a tile keeps its 16-byte chunk c in slot
+// c ^ swz(r) (2-byte keys: 256-byte rows, swz(r) = r & 15; fp8: 128-byte
+// rows, swz(r) = (r >> 1) & 7), which keeps the B-operand reads free of bank
+// conflicts.  Scores collect in LDS and leave in one coalesced pass per wave
+// at the end.
+template <int KK> struct StreamGeom {
+  static constexpr int ROW = KK == KK_FP8 ? 128 : 256;   // bytes per key
+  static constexpr int TB = 32 * ROW;                     // bytes per tile
+  static constexpr int NLD = TB / 1024;                   // 1 KB loads per tile
+};
+
+template <int KK>
+constexpr size_t stream_lds_bytes(int chunk_tiles) {
+  return HIST_BINS * 4 + 4 * 2 * StreamGeom<KK>::TB + 4 * static_cast<size_t>(chunk_tiles) * 32 * 4;
+}
+
+template <int KK>
+struct StreamTile {   // one lane's share of a tile in flight: NLD x 16 bytes, plus its fp8 row scale
+  u32x4_t v[StreamGeom<KK>::NLD];
+  float sc;
+};
+
+template <int KK, int QK, int RB, int NQ>
+__global__ __launch_bounds__(256, 1) void score_stream_kernel(ScoreParams p) {
+  static_assert(KK == KK_BF16 || KK == KK_F16 || KK == KK_FP8, "1- or 2-byte keys");
+  using G = StreamGeom<KK>;
+  constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
+  extern __shared__ __align__(16) uint8_t s_raw[];
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_raw);
+  uint8_t* s_kt = s_raw + HIST_BINS * 4;                                  // [wave][2][TB]
+  float* s_out = reinterpret_cast<float*>(s_kt + 4 * 2 * G::TB);         // [wave][chunk_tiles * 32]
+
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 31, h2 = lane >> 5;
+  const int ncg = (p.n_chunks + 3) >> 2;
+  const int row32 = static_cast<int>(blockIdx.x) / ncg;   // rows * ncg < 2^31 (grid size)
+  const int64_t row = row32;
+  const int chunk = (static_cast<int>(blockIdx.x) - row32 * ncg) * 4 + wid;
+  const int s = row32 / p.n_q;
+  const bool active = chunk < p.n_chunks;
+  const int64_t u_begin = static_cast<int64_t>(chunk) * p.chunk_tiles * 32;
+  int64_t u_end = u_begin + static_cast<int64_t>(p.chunk_tiles) * 32;
+  if (u_end > p.n_units) u_end = p.n_units;
+
+  // load i of a tile covers the 1 KB of rows 1024 i / ROW ..; lane L takes
+  // the 16 bytes that belong at byte 16 L of it: row r = (1024 i + 16 L) / ROW,
+  // slot (16 L % ROW) / 16, holding chunk slot ^ swz(r)
+  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * G::ROW;
+  const float* sbase = KK == KK_FP8 ? p.k_scale + static_cast<int64_t>(s) * p.n_units : nullptr;
+  uint32_t loff[G::NLD];
+#pragma unroll
+  for (int i = 0; i < G::NLD; ++i) {
+    if constexpr (G::ROW == 256) {
+      const int r = 4 * i + (lane >> 4);
+      loff[i] = static_cast<uint32_t>(r) * 256u + 16u * ((lane & 15) ^ (r & 15));
+    } else {
+      const int r = 8 * i + (lane >> 3);
+      loff[i] = static_cast<uint32_t>(r) * 128u + 16u * ((lane & 7) ^ ((r >> 1) & 7));
+    }
+  }
+  auto load_tile = [&](StreamTile<KK>& tt, int j) __attribute__((always_inline)) {
+    const int64_t ut = u_begin + static_cast<int64_t>(j) * 32;
+    const char* tb = kbase + ut * G::ROW;
+    const int64_t lim = (p.n_units - ut) * G::ROW;   // bytes of the tile inside the cache
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i)
+      tt.v[i] = static_cast<int64_t>(loff[i]) < lim ? *reinterpret_cast<const u32x4_t*>(tb + loff[i])
+                                                    : u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (KK == KK_FP8) tt.sc = ut + n < p.n_units ? sbase[ut + n] : 0.f;
+  };
+  // The first NR tiles of the chunk are requested before anything else (the
+  // visible length is not known yet: tiles past it are loaded, never used),
+  // so that the keys stream while q is loaded and converted.
+  constexpr int NR = 4;
+  StreamTile<KK> rr[NR];
+  const int n_pre = active ? static_cast<int>((u_end - u_begin + 31) >> 5) : 0;   // tiles of the chunk
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+    if (k < n_pre) load_tile(rr[k], k);
+
+  const int32_t qpos = p.q_pos[row];
+  const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
+  u32x4_t qa[RB][8][NQ];
+  float wv[RB][16];
+  query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
+  for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = 0;
+
+  const int64_t n_vis = visible_tokens(qpos, kl, p.n_units * p.c) / p.c;
+  const int64_t c_end = n_vis < u_end ? n_vis : u_end;   // compute [u_begin, c_end)
+  const bool do_hist = n_vis > p.k_out;
+  const int64_t nf = (p.c == 1 && p.n_sink < n_vis) ? p.n_sink : (p.c == 1 ? n_vis : 0);
+  const int n_t = active && c_end > u_begin ? static_cast<int>((c_end - u_begin + 31) >> 5) : 0;
+
+  const uint32_t wbase = static_cast<uint32_t>(wid) * (2 * G::TB);
+  auto store_tile = [&](const StreamTile<KK>& tt, int buf) __attribute__((always_inline)) {
+    uint8_t* d = s_kt + wbase + buf * G::TB + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i) *reinterpret_cast<u32x4_t*>(d + 1024 * i) = tt.v[i];
+  };
+  float* so = s_out + wid * (p.chunk_tiles * 32);
+  auto compute = [&](int j, float sc) __attribute__((always_inline)) {
+    const uint8_t* kt = s_kt + wbase + (j & 1) * G::TB;
+    f32x16_t acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+    if constexpr (G::ROW == 256) {
+      uint32_t hx = 8u * h2;
+      asm volatile("" : "+v"(hx));
+      const uint8_t* kr = kt + n * 256;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(kr + 16u * ((hx + ks) ^ (n & 15)));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (F16OP) {
+            acc[rb] = mfma32x32x16_f16(qa[rb][ks][0], bh, acc[rb]);
+          } else {
+            acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bh, acc[rb]);
+            if constexpr (NQ == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][NQ - 1], bh, acc[rb]);
+          }
+        }
+      }
+    } else {
+      uint32_t hx = 4u * h2;
+      asm volatile("" : "+v"(hx));
+      const uint8_t* kr = kt + n * 128;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + 16u * ((hx + kk) ^ ((n >> 1) & 7)));
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const u32x2_t ca = fp8x4_to_f16x4_scaled(half ? v.z : v.x);
+          const u32x2_t cb = fp8x4_to_f16x4_scaled(half ? v.w : v.y);
+          const u32x4_t bh = u32x4_t{ca.x, ca.y, cb.x, cb.y};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32x32x16_f16(qa[rb][2 * kk + half][0], bh, acc[rb]);
+        }
+      }
+    }
+    // epilogue: ReLU, head weight, head sum
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) part[jj & 3] = fmaf(wv[rb][jj], relu(acc[rb][jj]), part[jj & 3]);
+    float tot = half_sum((part[0] + part[1]) + (part[2] + part[3]));
+    if constexpr (KK == KK_FP8) tot *= sc;
+    const int64_t u = u_begin + static_cast<int64_t>(j) * 32 + n;
+    const float val = u < n_vis ? tot : NEG_INF;
+    if (h2 == 0) {
+      so[j * 32 + n] = val;
+      if (do_hist && u >= nf && u < n_vis) atomicAdd(&s_hist[order_key(val) >> 20], 1u);
+    }
+  };
+
+  // tile j + k sits in LDS buffer k & 1 (j a multiple of NR, NR even); the
+  // NR tiles after the next one are in flight in the register ring
+  float scb[2] = {0.f, 0.f};   // fp8 scales of the tiles in the LDS buffers
+  __syncthreads();   // the histogram is clear
+  if (n_t > 0) {
+    store_tile(rr[0], 0);
+    scb[0] = rr[0].sc;
+    if (NR < n_t) load_tile(rr[0], NR);
+  }
+  auto step = [&](auto kc, int j) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int k1 = (k + 1) % NR;
+    const int jj = j + k;
+    if (jj >= n_t) return;
+    if (jj + 1 < n_t) {
+      store_tile(rr[k1], (k + 1) & 1);   // over tile jj - 1, read by the previous step
+      scb[(k + 1) & 1] = rr[k1].sc;
+    }
+    if (jj + 1 + NR < n_t) load_tile(rr[k1], jj + 1 + NR);
+    compute(jj, scb[k & 1]);
+  };
+  for (int j = 0; j < n_t; j += NR) {
+    step(std::integral_constant<int, 0>{}, j);
+    step(std::integral_constant<int, 1>{}, j);
+    step(std::integral_constant<int, 2>{}, j);
+    step(std::integral_constant<int, 3>{}, j);
+  }
+  // write-out of the wave's chunk: computed tiles, then -inf for the
+  // invisible rest when asked
+  if (active) {
+    const int64_t done = u_begin + static_cast<int64_t>(n_t) * 32 < u_end ? u_begin + static_cast<int64_t>(n_t) * 32
+                                                                         : u_end;
+    const int64_t w_end = p.fill_invisible ? u_end : done;
+    float* orow = p.scores + row * p.n_units;
+    for (int64_t u = u_begin + lane; u < w_end; u += 64) {
+      const int i = static_cast<int>(u - u_begin);
+      orow[u] = i < n_t * 32 ? so[i] : NEG_INF;
+    }
+  }
+  __syncthreads();
+  uint32_t* g = p.hist + row * HIST_BINS;
+  for (int b = threadIdx.x; b < HIST_BINS; b += 256) {
+    const uint32_t v = s_hist[b];
+    if (v) atomicAdd(g + b, v);
+  }
+}
+
 // Generic path: any element types, H <= 128, D <= 256.  One thread per
 // (row, unit); the row's (rotated) query and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
@@ -522,6 +734,33 @@ static bool scores_use_tiled(const ScoreParams& p) {
          p.chunk_tiles <= SC_MAX_TILES && p.n_units < (int64_t(1) << 24);   // 32-bit row offsets
 }
 
+// the decode stream kernel covers 1- and 2-byte keys on rows with the histogram
+static bool scores_use_stream(const ScoreParams& p) {
+  return (p.k_dtype == DSA_BF16 || p.k_dtype == DSA_F16 || p.k_dtype == DSA_FP8_E4M3) && p.hist != nullptr &&
+         p.chunk_major && p.chunk_tiles <= 32 && p.n_units < (int64_t(1) << 24);   // 32-bit row offsets
+}
+
+template <int KK, int QK, int NQ>
+static hipError_t launch_stream_rb(const ScoreParams& p, dim3 grid, hipStream_t st) {
+  const size_t lds = stream_lds_bytes<KK>(p.chunk_tiles);
+  static bool attr = false;
+  if (!attr) {
+    const int mx = static_cast<int>(stream_lds_bytes<KK>(32));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 1, NQ>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 2, NQ>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  if (p.H <= 32)
+    hipLaunchKernelGGL((score_stream_kernel<KK, QK, 1, NQ>), grid, dim3(256), lds, st, p);
+  else
+    hipLaunchKernelGGL((score_stream_kernel<KK, QK, 2, NQ>), grid, dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
 template <int KK, int QK, int NQ>
 static hipError_t launch_tiled_rb(const ScoreParams& p, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
@@ -540,6 +779,13 @@ template <int KK>
 static hipError_t launch_mfma_q(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t st) {
   constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
   const bool split = !F16OP && (p.q_dtype != DSA_BF16 || p.hadamard);
+  if constexpr (KK == KK_BF16 || KK == KK_F16 || KK == KK_FP8) {
+    if (scores_use_stream(p)) {
+      if (p.q_dtype == DSA_BF16)
+        return split ? launch_stream_rb<KK, 0, 2>(p, grid, st) : launch_stream_rb<KK, 0, 1>(p, grid, st);
+      return split ? launch_stream_rb<KK, 1, 2>(p, grid, st) : launch_stream_rb<KK, 1, 1>(p, grid, st);
+    }
+  }
   if constexpr (KK == KK_BF16 || KK == KK_F16) {
     if (scores_use_tiled(p)) {
       if (p.q_dtype == DSA_BF16)

@@ -15,6 +15,8 @@ sum_h |w| relu(q_h . k), which equals |s| for non-negative weights):
 
 import math
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -396,6 +398,23 @@ def test_forward_matches_oracle_small(n):
     wl = inputs.mini(n)
     x = inputs.generate(wl)
     _end_to_end(wl, x, dev(x), _rows_sample(wl, 32, seed=n))
+
+
+DECODE_STREAM_CASES = {
+    # few long rows: the scores go through the decode stream kernel and its
+    # fused histogram (f16 and bf16 keys; fp8 keys are the long-decode mini)
+    "f16_keys_ragged": lambda: replace(inputs.mini(3), name="dec_f16", S=3, n_kv=7001, q_pos0=7000, seed=91),
+    "bf16_keys_ragged": lambda: replace(inputs.mini(3), name="dec_bf16", S=2, n_kv=6500, q_pos0=6499,
+                                        k_dtype=torch.bfloat16, seed=92),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_STREAM_CASES))
+def test_forward_decode_stream_matches_oracle(case):
+    wl = DECODE_STREAM_CASES[case]()
+    x = inputs.generate(wl)
+    x["kv_len"] = torch.tensor([wl.n_kv - 37 * s for s in range(wl.S)], dtype=torch.int32)
+    _end_to_end(wl, x, dev(x), [(s, 0) for s in range(wl.S)])
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
