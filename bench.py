@@ -23,6 +23,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+CSRC = os.path.join(ROOT, "sparse_top_attention_indexer_amd")
+PROFILES = os.path.join(ROOT, "profiles")
 PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
 
 
@@ -37,6 +39,46 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------ kernel names, traffic
+
+def score_kernel_name(wl):
+    """The score kernel the library picks for this workload (its launch rules)."""
+    import torch
+    n_units = wl.n_kv // wl.c
+    rows = wl.S * wl.n_q
+    if wl.k_dtype == torch.float32 and wl.q_dtype == torch.float32:
+        return "score_valu_kernel"
+    if wl.c > 1:
+        return "score_mfma_kernel"   # pooled block keys are f32
+    multiblock = n_units > 16384 or (rows < 128 and n_units > 4096)
+    if multiblock and wl.k_dtype != torch.float32:
+        return "score_stream_kernel"
+    if wl.k_dtype in (torch.bfloat16, torch.float16) and wl.n_q % 4 == 0:
+        return "score_tiled_kernel"
+    return "score_mfma_kernel"
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record (calibrated by a copy of known
+    size), or None when there is none or the kernel's sources changed since."""
+    import glob
+    import hashlib
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*_traffic.md"))):
+        for line in open(f):
+            if not line.startswith("traffic-record: "):
+                continue
+            rec = json.loads(line[len("traffic-record: "):])
+            if rec["workload"] != workload or rec["kernel"] != kernel:
+                continue
+            h = hashlib.sha256()
+            for src in rec["sources"]:
+                with open(os.path.join(CSRC, src), "rb") as fh:
+                    h.update(fh.read())
+            return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
+    return None
 
 
 # ------------------------------------------------------------ algorithmic work
@@ -202,9 +244,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": ph["bytes"] / t_dom / 1e9, "peak": ph["peak"] / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = {"scores": "score_mfma_kernel", "topk": "topk kernels", "attn":
+    roof["kernel"] = {"scores": score_kernel_name(wl), "topk": "topk kernels", "attn":
                       {"mla": "attn_mla_kernel", "gqa": "attn_gqa_kernel", "f32": "attn_f32_kernel"}[wl.attn]}[dom]
+    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["launch_ms"] = ph["ms"]
 
     q_tokens = wl.S * wl.n_q

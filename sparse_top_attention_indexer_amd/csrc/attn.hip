@@ -21,7 +21,7 @@
 // Kernels:
 //   attn_f32_kernel   f32 Q/K/V, any head grouping, Dk, Dv <= 256 (VALU)
 //   attn_mla_kernel   MLA: 576-wide latent K, V = its first 512 columns, bf16,
-//                     32 heads per wave on 32x32x16 MFMAs
+//                     8 waves x 16 heads on 16x16x32 MFMAs
 //   attn_gqa_kernel   GQA: Dk = Dv = 128, up to 16 heads per KV group, bf16,
 //                     one wave per KV group on 16x16x32 MFMAs
 #include <type_traits>
