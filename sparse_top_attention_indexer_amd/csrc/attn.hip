@@ -262,13 +262,16 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   auto tokens_of = [&](int u) __attribute__((always_inline)) -> int32_t {
     return s_tok[(u * TILE + (lane & 31)) & (TOK_RING - 1)];
   };
-  // The gather of a tile is issued by waves 4..7 only, in the segment where
-  // they compute scores, one load between every four score products (they
-  // would otherwise stall the wave that issues them).  Wave 4 + l loads the
-  // 1 KB main parts of rows l, l + 4, ..., l + 28 (k = 0..7) and the rope parts
-  // of rows 8 l .. 8 l + 7 (k = 8).  The token ids come in two registers read
-  // from the ring a segment earlier: lane r of tl holds the token of row r,
-  // lane L of t8 that of row 8 l + L / 8.
+  // Each group gathers its part of a tile in its score segments, spread
+  // between the products (a load stalls the wave that issues it; the other
+  // group's products keep the SIMD busy meanwhile).  Waves 4 + l load the 1 KB
+  // main parts of rows l, l + 4, l + 8, l + 12 (k = 0..3) and the rope parts
+  // of rows 8 l .. 8 l + 7 (k = 8) of tile u + 2 in segment 2 u + 1; waves l
+  // load the main parts of rows l + 16, ..., l + 28 (k = 4..7) of tile u + 1 in
+  // segment 2 u.  A group waits for its own loads at the end of the next
+  // segment (waves 4..7 at even segment ends, waves 0..3 at odd ones).  The
+  // token ids come in registers read from the ring beforehand: lane r of tl
+  // holds the token of row r, lane L of t8 that of row 8 l + L / 8.
   const int gl = wid & 3;
   auto gather_tokens = [&](int u, int32_t& tl, int32_t& t8) __attribute__((always_inline)) {
     tl = tokens_of(u);
@@ -325,8 +328,11 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       if (i + SD < 36) kf[i % SD] = frag(i + SD);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // and one LDS read, in turn
-      if constexpr (decltype(with_gather)::value)
-        if ((i & 3) == 3) gather_k(i >> 2, tl, t8, lb, ln);
+      constexpr int plan = decltype(with_gather)::value;   // 0: none, 1: waves 4..7, 2: waves 0..3
+      if constexpr (plan == 1)
+        if (i % 7 == 6) gather_k(i < 28 ? i / 7 : 8, tl, t8, lb, ln);   // k = 0, 1, 2, 3, the rope
+      if constexpr (plan == 2)
+        if (i % 9 == 8) gather_k(4 + i / 9, tl, t8, lb, ln);            // k = 4..7
     }
   };
   // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
@@ -450,23 +456,28 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
     }
   };
   auto segment_end = [&](int sg) __attribute__((always_inline)) {
-    if ((sg & 1) == 0) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): gather of tile sg / 2 + 2 has landed
+    if ((sg & 1) == (grp == 0 ? 1 : 0)) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this group's loads have landed
     __syncthreads();
   };
   // Segment sg: waves 0..3 compute the scores and softmax of tile sg / 2
   // (even sg) or its PV products (odd sg); waves 4..7 do the same one segment
-  // later and gather tile sg / 2 + 2 in their score segments.  Waves without
+  // later.  Waves without
   // heads (Hq < 128) run the same products on zero queries, so that every wave
   // takes the same straight-line path.
-  using yes = std::true_type;
-  using no = std::false_type;
+  using plan_hi = std::integral_constant<int, 1>;   // the gather share of waves 4..7
+  using plan_lo = std::integral_constant<int, 2>;   // the gather share of waves 0..3
   if (grp == 0) {
     for (int u = 0; u < n_tiles; ++u) {
       segment_io(2 * u);
       f32x4_t s0, s1;
       u32x4_t ph, pl;
-      scores(no{}, u % KT_NBUF, s0, s1, 0, 0, 0);
+      // tile u + 1 past tile 1 (the first two come whole from the prologue;
+      // at u = 0 this reloads rows of tile 1 with the same bytes, and past
+      // the stream it loads rows nothing reads)
+      __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
+      scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), 0, (u + 1) % KT_NBUF);
       rescale(softmax(s0, s1, live_of(u), ph, pl));
+      __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u);
       segment_io(2 * u + 1);
       pv(u % KT_NBUF, ph, pl);
@@ -484,8 +495,10 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       segment_io(2 * u + 1);
       f32x4_t s0, s1;
       u32x4_t ph, pl;
-      scores(yes{}, u % KT_NBUF, s0, s1, g_tl, g_t8, (u + 2) % KT_NBUF);
+      __builtin_amdgcn_s_setprio(2);
+      scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, g_t8, (u + 2) % KT_NBUF);
       rescale(softmax(s0, s1, live_of(u), ph, pl));
+      __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u + 1);
       segment_io(2 * u + 2);
       gather_tokens(u + 3, g_tl, g_t8);   // for the next score segment
