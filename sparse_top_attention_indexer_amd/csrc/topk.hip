@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
     uint32_t prefix = b1 << 20, pmask = 0xfff00000u;
     const int shifts[2] = {8, 0};
     const int nbits[2] = {12, 8};
+    uint32_t n_eq = 0;   // candidates whose key equals T
     for (int pass = 0; pass < 2; ++pass) {
       const int nb = 1 << nbits[pass], sh = shifts[pass];
       for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
@@ -283,14 +284,19 @@ __global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
       need -= above;
       prefix |= b << sh;
       pmask |= static_cast<uint32_t>(nb - 1) << sh;
+      if (pass == 1) n_eq = s_hist[b];   // read before the next pass clears the bins
     }
     T = prefix;
+    __syncthreads();
     // the need-th smallest index among candidates equal to T: radix select on
-    // the complemented index (largest complement = smallest index), 3 x 11 bits
+    // the complemented index (largest complement = smallest index), 3 x 11 bits;
+    // when every candidate equal to T is kept (no tie is cut, the usual
+    // case), the largest index does
+    const bool cut = n_eq > need;
     uint32_t jp = 0, jm = 0;
     const int jsh[3] = {21, 10, 0};
     const int jbits[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = 0; pass < (cut ? 3 : 0); ++pass) {
       const int nb = 1 << jbits[pass], sh = jsh[pass];
       for (int b = tid; b < HIST_BINS; b += 256) s_hist[b] = 0;
       __syncthreads();
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
       jp |= b << sh;
       jm |= static_cast<uint32_t>(nb - 1) << sh;
     }
-    J = ~jp;
+    J = cut ? ~jp : 0xffffffffu;
   }
   // per-chunk counts of selected candidates, then output offsets
   for (int c = tid; c < p.n_chunks; c += 256) s_chunk[c] = 0;
