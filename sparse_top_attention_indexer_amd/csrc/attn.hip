@@ -530,33 +530,56 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
 // ============================================================== GQA kernel ==
 
 constexpr int GQA_D = 128;
-constexpr int GVROW = TILE + 4;
-constexpr size_t GQA_LDS = 4 * (GQA_D * GVROW) * 2 + TILE * 4 + 64 + MAX_BLOCKS * 4;
+constexpr int GQA_VT = TILE * GQA_D * 2;   // one V tile of one wave in LDS (8 KB)
+
+// LDS of a GQA workgroup: two V tiles per wave, the stream scratch, and the
+// row's block list in block mode
+static size_t gqa_lds_bytes(const AttnParams& p) {
+  return 4 * 2 * GQA_VT + 64 + (p.idx != nullptr && p.c > 1 ? static_cast<size_t>(p.k_sel) * 4 : 0);
+}
+
+struct GqaK {   // K fragments of one tile: key block mb, contraction step ks
+  u32x4_t a[2][4];
+};
+struct GqaV {   // one lane's share of a V tile: rows 4 i + lane / 16, 16-byte chunk lane % 16
+  u32x4_t v[8];
+};
 
 // One workgroup = one query row x one stream chunk x 4 KV groups; wave w owns
-// KV group g = 4 * blockIdx.y + w and its G <= 16 query heads (MFMA columns,
-// padded to 16).  K fragments come straight from the cache rows; each wave
-// transposes its V tile through a private LDS region.
+// KV group g = 4 * blockIdx.y + w and its G <= 16 query heads (the MFMA
+// columns, padded to 16).  After the stream set-up every wave runs its own
+// pipeline over tiles of 32 stream entries, with no workgroup barrier: the
+// token ids of tile j + 3 are fetched while tile j is computed; the K
+// fragments of tile j + 1 (A operand of S^T = K Q^T, straight from the cache
+// rows) and its V rows (coalesced, 1 KB per load) are in flight in registers;
+// the wave writes the V rows of tile j into one of its two LDS buffers and
+// reads them back transposed with ds_read_b64_tr_b16 as the A operand of
+// O^T = V^T P^T.  V row t keeps its 32-byte dim block b in slot b ^ (t & 7),
+// which keeps both the row writes and the transposing reads free of bank
+// conflicts.  With 8 heads per KV group the gathered K/V rows (16 KB per tile
+// and group) outweigh the products: the kernel is bound by L2 / last-level
+// cache bandwidth, not by the MFMAs.
 __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t s_raw[];
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  uint16_t* s_vt = reinterpret_cast<uint16_t*>(s_raw) + wid * (GQA_D * GVROW);
-  int32_t* s_tok = reinterpret_cast<int32_t*>(reinterpret_cast<uint16_t*>(s_raw) + 4 * GQA_D * GVROW);
-  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_tok + TILE);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* s_vt = s_raw + wid * (2 * GQA_VT);
+  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_raw + 4 * 2 * GQA_VT);
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);
 
   const int64_t row = blockIdx.x / p.n_split;
   const int sp = blockIdx.x % p.n_split;
   const int s = static_cast<int>(row / p.n_q);
-  const StreamInfo si = stream_setup<4>(p, row, s_blk, s_scr);
+  const StreamInfo si = stream_setup<4>(p, row, s_blk, s_scr);   // the last workgroup barrier
   int64_t p0, p1;
   split_range(p, sp, si.len, &p0, &p1);
+  const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
 
   const int G = p.Hq / p.Hkv;
   const int g = blockIdx.y * 4 + wid;
-  const bool gvalid = g < p.Hkv;
+  if (g >= p.Hkv) return;
   const int col = lane & 15, quad = lane >> 4;
-  const bool hvalid = gvalid && col < G;
+  const bool hvalid = col < G;
   const int head = g * G + col;
 
   u32x4_t qf[4];
@@ -571,51 +594,67 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
   for (int db = 0; db < 8; ++db) o[db] = f32x4_t{};
   float m_run = NEG_INF, l_run = 0.f;
   const float c2 = p.scale_log2;
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + s * p.k_seq + (gvalid ? g : 0) * p.k_head;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + s * p.v_seq + (gvalid ? g : 0) * p.v_head;
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + s * p.k_seq + g * p.k_head;
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + s * p.v_seq + g * p.v_head;
 
-  for (int64_t t0 = p0; t0 < p1; t0 += TILE) {
-    __syncthreads();   // s_tok of the previous tile is no longer read
-    if (tid < TILE) s_tok[tid] = static_cast<int32_t>(t0 + tid < p1 ? stream_token(p, row, si, s_blk, t0 + tid) : -1);
-    __syncthreads();
-    bool any = false;
-#pragma unroll
-    for (int r = 0; r < TILE; ++r) any |= s_tok[r] >= 0;
-    if (!any || !gvalid) continue;
-
-    // V tile: lane loads token (lane & 31), dims [64 * (lane >> 5), +64), writes V^T
-    {
-      const int vt = lane & 31, vh = lane >> 5;
-      const int64_t tok = s_tok[vt];
-      const uint16_t* vr = vbase + (tok >= 0 ? tok : 0) * p.v_tok + 64 * vh;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t v = tok >= 0 ? *reinterpret_cast<const u32x4_t*>(vr + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          s_vt[(64 * vh + 8 * i + jj) * GVROW + vt] = static_cast<uint16_t>(wv[jj >> 1] >> (16 * (jj & 1)));
-      }
-    }
-    // S^T = K (32 keys x 128) . Q^T (128 x 16 heads): two 16-key blocks
-    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+  // token id of entry lane % 32 of tile j (-1: dead or past the chunk)
+  auto tile_tokens = [&](int j) __attribute__((always_inline)) -> int32_t {
+    const int64_t pos = p0 + static_cast<int64_t>(j) * TILE + (lane & 31);
+    return pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
+  };
+  auto load_k = [&](GqaK& kk, int32_t tok) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int64_t tok = s_tok[16 * mb + col];
-      const uint16_t* kr = kbase + (tok >= 0 ? tok : 0) * p.k_tok;
+      const int32_t t = __shfl(tok, 16 * mb + col, 64);
+      const uint16_t* kr = kbase + static_cast<int64_t>(t >= 0 ? t : 0) * p.k_tok + 8 * quad;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t a = tok >= 0 ? *reinterpret_cast<const u32x4_t*>(kr + 32 * ks + 8 * quad) : u32x4_t{0u, 0u, 0u, 0u};
-        sacc[mb] = mfma16x16x32_bf16(a, qf[ks], sacc[mb]);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        kk.a[mb][ks] = t >= 0 ? *reinterpret_cast<const u32x4_t*>(kr + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    // accumulator (mb, j) holds key 16 mb + 4 quad + j of head column `col`
+  };
+  auto load_v = [&](GqaV& vv, int32_t tok) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int32_t t = __shfl(tok, 4 * i + (lane >> 4), 64);
+      const uint16_t* vr = vbase + static_cast<int64_t>(t >= 0 ? t : 0) * p.v_tok + 8 * col;
+      vv.v[i] = t >= 0 ? *reinterpret_cast<const u32x4_t*>(vr) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_v = [&](const GqaV& vv, int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 4 * i + (lane >> 4);
+      *reinterpret_cast<u32x4_t*>(s_vt + b * GQA_VT + t * 256 + 32 * ((col >> 1) ^ (t & 7)) + 16 * (col & 1)) =
+          vv.v[i];
+    }
+  };
+  // V^T fragment of dim block db from buffer b: source lane (quad, 4 m + r)
+  // addresses row R = 4 quad + m (then R + 16), dims 16 db + 4 r; the
+  // transposing read hands lane j of each 16-lane group dim 16 db + j of
+  // those four rows
+  const uint32_t vr_m = (lane >> 2) & 3, vr_r = lane & 3, vr_R = 4 * quad + vr_m;
+  auto vfrag = [&](int b, int db) __attribute__((always_inline)) -> u32x4_t {
+    uint8_t* ad = s_vt + b * GQA_VT + vr_R * 256 + 32 * (db ^ (vr_R & 7)) + 8 * vr_r;
+    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)ad);
+    const v4i16_t c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ad + 16 * 256));
+    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), c2_ = __builtin_bit_cast(u32x2_t, c);
+    return u32x4_t{a2.x, a2.y, c2_.x, c2_.y};
+  };
+  // scores, online softmax and PV products of the tile in buffer b
+  auto compute = [&](const GqaK& kk, int b, uint32_t live) __attribute__((always_inline)) {
+    // S^T = K (32 keys x 128) . Q^T (128 x 16 heads): two 16-key blocks;
+    // accumulator (mb, j) holds key 16 mb + 4 quad + j of head column col
+    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) sacc[mb] = mfma16x16x32_bf16(kk.a[mb][ks], qf[ks], sacc[mb]);
     float sv[8];
     float tmax = NEG_INF;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = 16 * (j >> 2) + 4 * quad + (j & 3);
-      sv[j] = s_tok[key] >= 0 ? sacc[j >> 2][j & 3] : NEG_INF;
+      sv[j] = (live >> key) & 1u ? sacc[j >> 2][j & 3] : NEG_INF;
       tmax = fmaxf(tmax, sv[j]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -636,11 +675,10 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       const float a = m_run == NEG_INF ? 0.f : exp2f(fmaf(sv[j], c2, -mb_));
-      const float b = m_run == NEG_INF ? 0.f : exp2f(fmaf(sv[j + 1], c2, -mb_));
-      pk[j >> 1] = pack_bf16x2(a, b);
-      pl[j >> 1] = pack_bf16x2(a - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] & 0xffffu)),
-                               b - bf16_to_f32(static_cast<uint16_t>(pk[j >> 1] >> 16)));
-      psum += a + b;
+      const float bb = m_run == NEG_INF ? 0.f : exp2f(fmaf(sv[j + 1], c2, -mb_));
+      pk[j >> 1] = pack_bf16x2(a, bb);
+      pl[j >> 1] = pack_bf16x2(a - __uint_as_float(pk[j >> 1] << 16), bb - __uint_as_float(pk[j >> 1] & 0xffff0000u));
+      psum += a + bb;
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
@@ -648,19 +686,46 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
     // P^T operand: slot (quad, j) <-> key 4 quad + j (j < 4), 16 + 4 quad + j - 4 (j >= 4)
     const u32x4_t pb = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
     const u32x4_t pr = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
-    __builtin_amdgcn_s_waitcnt(0);   // V^T writes of this wave are visible to its own reads
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* vr = s_vt + (16 * db + col) * GVROW + 4 * quad;
-      const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(vr);
-      const u32x2_t a1 = *reinterpret_cast<const u32x2_t*>(vr + 16);
-      const u32x4_t va = u32x4_t{a0.x, a0.y, a1.x, a1.y};
+      const u32x4_t va = vfrag(b, db);
       o[db] = mfma16x16x32_bf16(va, pb, o[db]);
       o[db] = mfma16x16x32_bf16(va, pr, o[db]);
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  GqaK kA, kB;
+  GqaV vA, vB;
+  int32_t tj = n_tiles > 0 ? tile_tokens(0) : -1;    // tokens of tile j
+  int32_t tj1 = n_tiles > 1 ? tile_tokens(1) : -1;   // of tile j + 1
+  int32_t tj2 = n_tiles > 2 ? tile_tokens(2) : -1;   // of tile j + 2
+  if (n_tiles > 0) {
+    load_k(kA, tj);
+    load_v(vA, tj);
   }
+  // one tile: its V rows into LDS buffer j & 1 (which held tile j - 2, read
+  // by this wave before), the loads of tile j + 1, the token ids of tile
+  // j + 3, then the products of tile j (fully dead tiles are skipped)
+  auto step = [&](const GqaK& kc, const GqaV& vc, GqaK& kn, GqaV& vn, int j) __attribute__((always_inline)) {
+    store_v(vc, j & 1);
+    if (j + 1 < n_tiles) {
+      load_k(kn, tj1);
+      load_v(vn, tj1);
+    }
+    const int32_t tj3 = j + 3 < n_tiles ? tile_tokens(j + 3) : -1;
+    const uint32_t live = static_cast<uint32_t>(__ballot(tj >= 0));
+    asm volatile("" ::: "memory");   // the V rows are in LDS before they are read back
+    if (live != 0u) compute(kc, j & 1, live);
+    tj = tj1;
+    tj1 = tj2;
+    tj2 = tj3;
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(kA, vA, kB, vB, j);
+    if (j + 1 >= n_tiles) break;
+    step(kB, vB, kA, vA, j + 1);
+  }
+
   if (!hvalid) return;
   // accumulator (db, j) holds dim 16 db + 4 quad + j of head column `col`
   if (p.n_split == 1) {
@@ -673,9 +738,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
   } else {
     float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(GQA_D);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pp[16 * db + 4 * quad + j] = o[db][j];
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * quad) = o[db];
     if (quad == 0) {
       pp[GQA_D] = m_run;
       pp[GQA_D + 1] = l_run;
@@ -905,12 +968,12 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
     static bool attr = false;
     if (!attr) {
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GQA_LDS));
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(4 * 2 * GQA_VT + 64 + MAX_BLOCKS * 4));
       if (e != hipSuccess) return e;
       attr = true;
     }
     hipLaunchKernelGGL(attn_gqa_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hkv + 3) / 4),
-                       dim3(256), GQA_LDS, st, p);
+                       dim3(256), gqa_lds_bytes(p), st, p);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(static_cast<unsigned>(rows * p.Hq * p.n_split)), dim3(64),
                        F32_LDS, st, p);
