@@ -489,8 +489,14 @@ struct StreamTile {   // one lane's share of a tile in flight: NLD x 16 bytes, p
   float sc;
 };
 
+// fp8 keys: tiles half the size, two workgroups per CU (two waves per SIMD,
+// so that one wave's fp8 conversion and epilogue overlap the other's
+// products) and a ring of two tiles; 2-byte keys: one workgroup per CU and a
+// ring of four tiles
+template <int KK> constexpr int stream_occupancy() { return KK == KK_FP8 ? 2 : 1; }
+
 template <int KK, int QK, int RB, int NQ>
-__global__ __launch_bounds__(256, 1) void score_stream_kernel(ScoreParams p) {
+__global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kernel(ScoreParams p) {
   static_assert(KK == KK_BF16 || KK == KK_F16 || KK == KK_FP8, "1- or 2-byte keys");
   using G = StreamGeom<KK>;
   constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void score_stream_kernel(ScoreParams p) {
   // The first NR tiles of the chunk are requested before anything else (the
   // visible length is not known yet: tiles past it are loaded, never used),
   // so that the keys stream while q is loaded and converted.
-  constexpr int NR = 4;
+  constexpr int NR = stream_occupancy<KK>() == 2 ? 2 : 4;
   StreamTile<KK> rr[NR];
   const int n_pre = active ? static_cast<int>((u_end - u_begin + 31) >> 5) : 0;   // tiles of the chunk
 #pragma unroll
@@ -646,8 +652,10 @@ __global__ __launch_bounds__(256, 1) void score_stream_kernel(ScoreParams p) {
   for (int j = 0; j < n_t; j += NR) {
     step(std::integral_constant<int, 0>{}, j);
     step(std::integral_constant<int, 1>{}, j);
-    step(std::integral_constant<int, 2>{}, j);
-    step(std::integral_constant<int, 3>{}, j);
+    if constexpr (NR == 4) {
+      step(std::integral_constant<int, 2>{}, j);
+      step(std::integral_constant<int, 3>{}, j);
+    }
   }
   // write-out of the wave's chunk: computed tiles, then -inf for the
   // invisible rest when asked
@@ -807,9 +815,15 @@ hipError_t launch_scores(ScoreParams p, hipStream_t st) {
     return hipGetLastError();
   }
   const int64_t n_tiles = (p.n_units + 31) / 32;
-  // Long rows: chunks of up to 32 tiles per wave; short rows spread over 4 waves.
+  // Long rows: chunks of up to 32 tiles per wave; short rows spread over 4
+  // waves; fp8 decode rows (two waves per SIMD) in chunks that give about
+  // 2048 waves.
   int64_t ct = (n_tiles + 3) / 4;
   if (ct > 32) ct = 32;
+  if (p.hist != nullptr && p.k_dtype == DSA_FP8_E4M3) {
+    const int64_t fill = (rows * n_tiles + 2047) / 2048;
+    if (ct > fill) ct = fill < 4 ? 4 : fill;
+  }
   if (ct < 1) ct = 1;
   p.chunk_tiles = static_cast<int32_t>(ct);
   p.n_chunks = static_cast<int32_t>((n_tiles + ct - 1) / ct);
