@@ -77,12 +77,16 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 // differs by 8 (15 vs 7), and e4m3 subnormals map to f16 subnormals the same way.
 // (The NaN code 0x7f maps to a finite value; stored keys never hold it.)
 __device__ __forceinline__ u32x2_t fp8x4_to_f16x4_scaled(uint32_t x) {
-  // spread bytes b0..b3 into the low bytes of four 16-bit lanes
-  const uint32_t lo = (x & 0xffu) | ((x & 0xff00u) << 8);          // [0, b1, 0, b0]
-  const uint32_t hi = ((x >> 16) & 0xffu) | ((x >> 8) & 0xff0000u); // [0, b3, 0, b2]
+  // spread bytes b0..b3 into the low bytes of four 16-bit lanes (byte
+  // permutes; selector 0x0c gives a zero byte)
+  const uint32_t lo = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);   // [0, b1, 0, b0]
+  const uint32_t hi = __builtin_amdgcn_perm(0u, x, 0x0c030c02u);   // [0, b3, 0, b2]
+  // per lane: (b + (b & 0x80)) << 7 = ((b & 0x7f) << 7) | ((b & 0x80) << 8),
+  // exponent and mantissa up by 7 bits and the sign to bit 15, with no carry
+  // out of the 16-bit lane
   u32x2_t r;
-  r.x = ((lo & 0x007f007fu) << 7) | ((lo & 0x00800080u) << 8);
-  r.y = ((hi & 0x007f007fu) << 7) | ((hi & 0x00800080u) << 8);
+  r.x = (lo + (lo & 0x00800080u)) << 7;
+  r.y = (hi + (hi & 0x00800080u)) << 7;
   return r;
 }
 
