@@ -184,20 +184,30 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
 }
 
 // Threshold bin per row; counts units above it per chunk; gathers the units
-// of the threshold bin as candidates.
+// of the threshold bin as candidates.  The chunk's keys (16 per thread) are
+// loaded first, so that their latency overlaps that of the row's position and
+// histogram, and stay in registers for both passes.
+static_assert(TOPK_CHUNK == 16 * 256, "16 keys per thread");
 __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   __shared__ uint32_t s_hist[HIST_BINS];
   __shared__ uint32_t s_scr[16];
-  __shared__ uint32_t s_cnt, s_base;
+  __shared__ uint32_t s_base;
   const int64_t row = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x % p.n_chunks;
+  const int64_t c0 = static_cast<int64_t>(ch) * TOPK_CHUNK;
+  const float* sc = p.scores + row * p.n_units;
+  uint32_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t j = c0 + 256 * i + threadIdx.x;
+    key[i] = j < p.n_units ? order_key(sc[j]) : 0u;
+  }
   const RowInfo ri = row_info(p, row);
   if (ri.n_vis <= p.k_out) return;
   const uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
   if (need == 0) return;
   const uint32_t* g = p.hist + row * HIST_BINS;
   for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = g[b];
-  if (threadIdx.x == 0) s_cnt = 0;
   __syncthreads();
   uint32_t above;
   const uint32_t b1 = find_bin_desc(s_hist, HIST_BINS, need, s_scr, &above);
@@ -205,16 +215,17 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
     p.thr[row * 4 + 0] = b1;
     p.thr[row * 4 + 3] = above;
   }
-  int64_t j0 = static_cast<int64_t>(ch) * p.chunk, j1 = j0 + p.chunk;
-  if (j0 < ri.nf) j0 = ri.nf;
-  if (j1 > ri.n_vis) j1 = ri.n_vis;
-  const float* sc = p.scores + row * p.n_units;
+  const int64_t j0 = c0 > ri.nf ? c0 : ri.nf;   // candidates: [j0, j1), past the forced sinks
+  const int64_t j1 = c0 + TOPK_CHUNK < ri.n_vis ? c0 + TOPK_CHUNK : ri.n_vis;
   // pass 1: count units above the bin and units in it
   uint32_t n_hi = 0, n_in = 0;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
-    const uint32_t bin = order_key(sc[j]) >> 20;
-    n_hi += bin > b1;
-    n_in += bin == b1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t j = c0 + 256 * i + threadIdx.x;
+    const bool in = j >= j0 && j < j1;
+    const uint32_t bin = key[i] >> 20;
+    n_hi += in && bin > b1;
+    n_in += in && bin == b1;
   }
   uint32_t tot_hi, tot_in;
   block_excl_scan_256(n_hi, s_scr, &tot_hi);
@@ -227,11 +238,12 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   // pass 2: write the candidates (key, index)
   uint32_t w = s_base + my_off;
   uint32_t* cand = p.cand + row * p.cand_cap * 2;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
-    const uint32_t k = order_key(sc[j]);
-    if ((k >> 20) == b1) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t j = c0 + 256 * i + threadIdx.x;
+    if (j >= j0 && j < j1 && (key[i] >> 20) == b1) {
       if (w < p.cand_cap) {
-        cand[2 * w] = k;
+        cand[2 * w] = key[i];
         cand[2 * w + 1] = static_cast<uint32_t>(j);
       }
       ++w;
@@ -333,34 +345,51 @@ __global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
   }
 }
 
-// Ordered compaction of one chunk of a row.
+// Ordered compaction of one chunk of a row: thread t owns the 16 units
+// 16 t .. 16 t + 15 of the chunk (loaded first, as four 16-byte loads), so an
+// exclusive scan of the per-thread counts gives ascending output positions.
 __global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
   __shared__ uint32_t s_scr[16];
   const int64_t row = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x % p.n_chunks;
+  const int64_t c0 = static_cast<int64_t>(ch) * TOPK_CHUNK;
+  const int64_t a0 = c0 + 16 * threadIdx.x;
+  const float* sc = p.scores + row * p.n_units;
+  float v[16];
+  if (a0 + 16 <= p.n_units && (p.n_units & 3) == 0) {   // whole, 16-byte aligned run
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(sc + a0 + 4 * i);
+      v[4 * i] = q[0];
+      v[4 * i + 1] = q[1];
+      v[4 * i + 2] = q[2];
+      v[4 * i + 3] = q[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = a0 + i < p.n_units ? sc[a0 + i] : 0.f;
+  }
+  const uint32_t T = p.thr[row * 4 + 1], J = p.thr[row * 4 + 2];
+  const uint32_t off = p.offs[row * p.n_chunks + ch];
   const RowInfo ri = row_info(p, row);
   if (ri.n_vis <= p.k_out || ri.K == ri.nf) return;
-  const uint32_t T = p.thr[row * 4 + 1], J = p.thr[row * 4 + 2];
-  int64_t j0 = static_cast<int64_t>(ch) * p.chunk, j1 = j0 + p.chunk;
-  if (j0 < ri.nf) j0 = ri.nf;
-  if (j1 > ri.n_vis) j1 = ri.n_vis;
-  const int64_t len = j1 > j0 ? j1 - j0 : 0;
-  const int64_t per = (len + 255) / 256;
-  const int64_t a0 = j0 + (threadIdx.x * per < len ? threadIdx.x * per : len);
-  const int64_t a1 = a0 + per < j1 ? a0 + per : j1;
-  const float* sc = p.scores + row * p.n_units;
-  uint32_t cnt = 0;
-  for (int64_t j = a0; j < a1; ++j) {
-    const uint32_t k = order_key(sc[j]);
-    cnt += (k > T || (k == T && static_cast<uint32_t>(j) <= J));
+  const int64_t j0 = c0 > ri.nf ? c0 : ri.nf;
+  const int64_t j1 = c0 + TOPK_CHUNK < ri.n_vis ? c0 + TOPK_CHUNK : ri.n_vis;
+  uint32_t sel = 0;   // bit i: unit a0 + i is kept
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t j = a0 + i;
+    const uint32_t k = order_key(v[i]);
+    const bool keep = j >= j0 && j < j1 && (k > T || (k == T && static_cast<uint32_t>(j) <= J));
+    sel |= static_cast<uint32_t>(keep) << i;
   }
   uint32_t tot;
-  uint32_t pos = p.offs[row * p.n_chunks + ch] + block_excl_scan_256(cnt, s_scr, &tot);
+  uint32_t pos = off + block_excl_scan_256(__builtin_popcount(sel), s_scr, &tot);
   int32_t* out = p.idx + row * p.k_out;
-  for (int64_t j = a0; j < a1; ++j) {
-    const uint32_t k = order_key(sc[j]);
-    if (k > T || (k == T && static_cast<uint32_t>(j) <= J)) {
-      if (pos < ri.K) out[pos] = static_cast<int32_t>(j);   // guard: never past K
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if ((sel >> i) & 1u) {
+      if (pos < ri.K) out[pos] = static_cast<int32_t>(a0 + i);   // guard: never past K
       ++pos;
     }
   }
