@@ -255,6 +255,36 @@ def test_dense_attention_matches_oracle(n):
     assert err <= _attn_tol(wl)
 
 
+def test_gqa_token_mode_uneven_groups_split_streams():
+    """GQA in token mode: 6 KV groups (the second workgroup row has waves
+    without a group), 4 heads per group (MFMA columns padded to 16), lists
+    with dead entries, streams split over several workgroups, f32 and bf16
+    output."""
+    bf = torch.bfloat16
+    wl = inputs.Workload("gqa6", 2, 5, 3000, 2990, 16, 128, bf, bf, "normal", 0.25, 700, 1, 0,
+                         False, "gqa", 24, 6, 128, 128, bf, 128 ** -0.5, seed=81)
+    x = inputs.generate(wl)
+    x["kv_len"] = torch.tensor([3000, 2500], dtype=torch.int32)
+    idx, _ = _oracle_idx(x, wl)
+    idx[0, 1, ::7] = -1
+    idx[1, 3, 100:200] = -1
+    d = dev(x)
+    idx_d = torch.from_numpy(idx).to(torch.int32).to(DEV)
+    rows = [(s, i) for s in range(wl.S) for i in range(wl.n_q)]
+    ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), idx, x["q_pos"].numpy(),
+                             x["kv_len"].numpy(), 1, wl.scale, rows)
+    got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], idx_d, kv_len=d["kv_len"],
+                          scale=wl.scale).cpu().double().numpy()
+    err = max(float(np.abs(got[s, i] - ref[s, i]).max()) for s, i in rows)
+    print(f"gqa token mode: max |O - oracle| {err:.2e}")
+    assert err <= 2e-2
+    got16 = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], idx_d, kv_len=d["kv_len"],
+                            scale=wl.scale, o_dtype=torch.bfloat16).cpu().double().numpy()
+    for s, i in rows:
+        r = ref[s, i]
+        assert np.all(np.abs(got16[s, i] - r) <= 2e-2 * np.maximum(1.0, np.abs(r)))
+
+
 def test_attention_bf16_output_and_empty_rows():
     wl = inputs.mini(2)
     x = inputs.generate(wl)
