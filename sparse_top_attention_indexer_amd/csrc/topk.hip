@@ -46,23 +46,38 @@ __device__ __forceinline__ RowInfo row_info(const TopkParams& p, int64_t row) {
 // Returns b and sets *above.  All threads get the result.
 __device__ uint32_t find_bin_desc(const uint32_t* hist, int nb, uint32_t need, uint32_t* scratch,
                                   uint32_t* above) {
-  const int per = nb / 256;
-  // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 owns the top bins
+  // thread t owns bins [nb - (t+1)*per, nb - t*per): thread 0 owns the top
+  // bins; its counts are read once (into registers: the search below then
+  // needs no dependent LDS reads)
+  const int per = nb / 256;   // 1, 4, 8 or 16
   const int hi = nb - threadIdx.x * per;
+  uint32_t c[16];
   uint32_t local = 0;
-  for (int b = hi - per; b < hi; ++b) local += hist[b];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c[i] = i < per ? hist[hi - 1 - i] : 0u;   // c[i]: the i-th bin from the top of the thread's range
+    local += c[i];
+  }
   uint32_t total;
   const uint32_t excl = block_excl_scan_256(local, scratch, &total);  // elements in higher bins
   if (excl < need && need <= excl + local) {
     uint32_t acc = excl;
-    for (int b = hi - 1; b >= hi - per; --b) {
-      if (acc + hist[b] >= need) {
-        scratch[4] = static_cast<uint32_t>(b);
-        scratch[5] = acc;
-        break;
+    int found = per - 1;
+    uint32_t acc_at = 0;
+    bool done = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (!done && i < per) {
+        if (acc + c[i] >= need) {
+          found = i;
+          acc_at = acc;
+          done = true;
+        }
+        acc += c[i];
       }
-      acc += hist[b];
     }
+    scratch[4] = static_cast<uint32_t>(hi - 1 - found);
+    scratch[5] = acc_at;
   }
   __syncthreads();
   const uint32_t bin = scratch[4];
@@ -73,11 +88,16 @@ __device__ uint32_t find_bin_desc(const uint32_t* hist, int nb, uint32_t need, u
 
 // ------------------------------------------------------- one-row-per-block --
 
+// Candidate e of a row lives at s_key[e + e / 16]: the padding word after
+// every 16 keys makes the compaction's reads (thread t reads its contiguous
+// run 16 t .. 16 t + 15, words 17 t + i) free of bank conflicts.
+__device__ __forceinline__ int64_t key_slot(int64_t e) { return e + (e >> 4); }
+
 __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   extern __shared__ uint32_t s_mem[];
   uint32_t* s_hist = s_mem;                 // HIST_BINS
   uint32_t* s_scr = s_mem + HIST_BINS;      // 16
-  uint32_t* s_key = s_scr + 16;             // row keys
+  uint32_t* s_key = s_scr + 16;             // row keys, padded (key_slot)
   const int64_t row = blockIdx.x;
   const RowInfo ri = row_info(p, row);
   int32_t* out = p.idx + row * p.k_out;
@@ -90,7 +110,7 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   const int64_t m = ri.n_vis - ri.nf;             // candidates: units nf .. n_vis-1
   const uint32_t need0 = static_cast<uint32_t>(ri.K - ri.nf);
   const float* sc = p.scores + row * p.n_units + ri.nf;
-  for (int64_t e = tid; e < m; e += 256) s_key[e] = order_key(sc[e]);
+  for (int64_t e = tid; e < m; e += 256) s_key[key_slot(e)] = order_key(sc[e]);
   for (int64_t j = tid; j < p.k_out; j += 256) {
     if (j < ri.nf) out[j] = static_cast<int32_t>(j);
     else if (j >= ri.K) out[j] = -1;
@@ -108,7 +128,7 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
     for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
     __syncthreads();
     for (int64_t e = tid; e < m; e += 256) {
-      const uint32_t k = s_key[e];
+      const uint32_t k = s_key[key_slot(e)];
       if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
@@ -126,7 +146,7 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   const int64_t e1 = e0 + per < m ? e0 + per : m;
   uint32_t n_gt = 0, n_eq = 0;
   for (int64_t e = e0; e < e1; ++e) {
-    const uint32_t k = s_key[e];
+    const uint32_t k = s_key[key_slot(e)];
     n_gt += k > T;
     n_eq += k == T;
   }
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   const uint32_t pos0 = block_excl_scan_256(n_gt + take_eq, s_scr, &tot);
   uint32_t pos = static_cast<uint32_t>(ri.nf) + pos0, eq_seen = 0;
   for (int64_t e = e0; e < e1; ++e) {
-    const uint32_t k = s_key[e];
+    const uint32_t k = s_key[key_slot(e)];
     bool keep = k > T;
     if (k == T) {
       keep = eq_seen < take_eq;
@@ -440,7 +460,7 @@ hipError_t launch_topk_clear(const TopkParams& p, hipStream_t st) {
 hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   if (!topk_use_multiblock(rows, p.n_units)) {
-    const size_t lds = (HIST_BINS + 16 + static_cast<size_t>(p.n_units)) * sizeof(uint32_t);
+    const size_t lds = (HIST_BINS + 16 + static_cast<size_t>(p.n_units + p.n_units / 16 + 1)) * sizeof(uint32_t);
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

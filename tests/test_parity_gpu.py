@@ -184,6 +184,15 @@ def test_topk_rows_in_lds_with_ties_and_sink():
     _topk_case(1, 8, 4000, 300, kind="equal", seed=2)
 
 
+def test_topk_rows_in_registers_long_rows():
+    """Rows of 4097..16384 units on the one-workgroup-per-row path (32 and 64
+    keys per thread), causal positions, ties and sinks."""
+    n = 6000
+    _topk_case(1, 128, n, 700, q_pos=torch.arange(n - 128, n, dtype=torch.int32)[None] - 900, seed=11)
+    _topk_case(1, 130, 12000, 1000, n_sink=2, kind="ties", seed=12)
+    _topk_case(1, 128, 16384, 4096, kind="equal", seed=13)
+
+
 def test_topk_multiblock_decode_rows():
     _topk_case(3, 1, 40000, 2048, n_sink=1, kv_len=[40000, 25000, 1000], seed=3)
     _topk_case(2, 1, 131072, 2048, seed=4)
