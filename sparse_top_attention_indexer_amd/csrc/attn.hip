@@ -183,7 +183,9 @@ __device__ __forceinline__ float quad_sum(float x) {
 // PV products.  Tiles are gathered with direct global -> LDS loads two
 // segments ahead (three tile buffers).  Token ids of the stream sit in an LDS
 // ring of 32 tiles, refilled 16 tiles ahead.
-__global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams p) {
+  constexpr int NW = MLA_WAVES;
+  constexpr int GW = NW / 2;   // waves per group
   extern __shared__ __align__(16) uint8_t s_raw[];
   uint8_t* s_kb = s_raw;                                                      // KT_NBUF tiles
   int32_t* s_tok = reinterpret_cast<int32_t*>(s_raw + KT_NBUF * KT_BYTES);   // token ring
@@ -196,9 +198,9 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   const int64_t row = rows - 1 - blockIdx.x / p.n_split;     // latest (longest causal) rows first
   const int sp = blockIdx.x % p.n_split;
   const int s = static_cast<int>(row / p.n_q);
-  const int grp = wid >> 2;
+  const int grp = wid / GW;
   const int col = lane & 15, q = lane >> 4;
-  const int head0 = blockIdx.y * 128 + wid * 16;
+  const int head0 = blockIdx.y * (16 * NW) + wid * 16;
   const bool wvalid = head0 < p.Hq;   // Hq is a multiple of 16
   const int head = head0 + col;
 
@@ -218,14 +220,14 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
     }
   }
 
-  const StreamInfo si = stream_setup<MLA_WAVES>(p, row, s_blk, s_scr);
+  const StreamInfo si = stream_setup<NW>(p, row, s_blk, s_scr);
   int64_t p0, p1;
   split_range(p, sp, si.len, &p0, &p1);
   // The token ring takes the first TOK_RING stream entries.  In token mode
   // the trailing dead entries (the -1 padding of short selections) are cut
   // off in the same pass over the index row; they would add nothing.
   uint32_t last = 0;   // 1 + offset of the last live entry
-  for (int i = tid; i < TOK_RING; i += 64 * MLA_WAVES) {
+  for (int i = tid; i < TOK_RING; i += 64 * NW) {
     const int32_t t = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
     s_tok[i] = t;
     if (t >= 0) last = static_cast<uint32_t>(i + 1);
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   const bool trim = p.idx != nullptr && p.c == 1 && p1 > p0;
   if (trim) {
     const int32_t* ir = p.idx + row * p.k_sel;
-    for (int64_t e = p0 + TOK_RING + tid; e < p1; e += 64 * MLA_WAVES) {
+    for (int64_t e = p0 + TOK_RING + tid; e < p1; e += 64 * NW) {
       const int32_t v = ir[e];
       if (v >= 0 && v < si.n_vis) last = static_cast<uint32_t>(e - p0 + 1);
     }
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   if (trim) {
     uint32_t e = 0;
 #pragma unroll
-    for (int w = 0; w < MLA_WAVES; ++w) e = max(e, s_scr[8 + w]);
+    for (int w = 0; w < NW; ++w) e = max(e, s_scr[8 + w]);
     p1 = p0 + e;
   }
   const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
@@ -264,30 +266,40 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   };
   // Each group gathers its part of a tile in its score segments, spread
   // between the products (a load stalls the wave that issues it; the other
-  // group's products keep the SIMD busy meanwhile).  Waves 4 + l load the 1 KB
-  // main parts of rows l, l + 4, l + 8, l + 12 (k = 0..3) and the rope parts
-  // of rows 8 l .. 8 l + 7 (k = 8) of tile u + 2 in segment 2 u + 1; waves l
-  // load the main parts of rows l + 16, ..., l + 28 (k = 4..7) of tile u + 1 in
-  // segment 2 u.  A group waits for its own loads at the end of the next
-  // segment (waves 4..7 at even segment ends, waves 0..3 at odd ones).  The
-  // token ids come in registers read from the ring beforehand: lane r of tl
-  // holds the token of row r, lane L of t8 that of row 8 l + L / 8.
-  const int gl = wid & 3;
-  auto gather_tokens = [&](int u, int32_t& tl, int32_t& t8) __attribute__((always_inline)) {
-    tl = tokens_of(u);
-    t8 = s_tok[(u * TILE + 8 * gl + (lane >> 3)) & (TOK_RING - 1)];
+  // group's products keep the SIMD busy meanwhile).  Wave l of the second
+  // group loads the 1 KB main parts of rows l, l + GW, ... below 16 and the
+  // rope parts of rows (32 / GW) l .. (32 / GW) (l + 1) - 1 of tile u + 2 in
+  // segment 2 u + 1; wave l of the first group loads the main parts of rows
+  // 16 + l, 16 + l + GW, ... of tile u + 1 in segment 2 u.  A group waits
+  // for its own loads at the end of the next segment (the second group at
+  // even segment ends, the first at odd ones).  The token ids come in a
+  // register read from the ring beforehand: lane r of tl holds the token of
+  // row r.
+  const int gl = wid % GW;
+  constexpr int N_MAIN = 16 / GW;   // main-part loads per wave and half tile
+  constexpr int N_ROPE = 4 / GW;    // rope loads per wave and tile (8 rows each)
+  auto gather_main = [&](int r, int32_t tl, uint32_t lb, int ln) __attribute__((always_inline)) {
+    const int32_t tk = __builtin_amdgcn_readlane(tl, r);
+    const char* src = kseq_b + static_cast<uint64_t>(tk > 0 ? tk : 0) * pitch;
+    dma16(src, (16u * ln) ^ (16u * main_swz(r)), lb + 1024u * r);
   };
-  auto gather_k = [&](int k, int32_t tl, int32_t t8, uint32_t lb, int ln) __attribute__((always_inline)) {
-    if (k < 8) {
-      const int r = gl + 4 * k;
-      const int32_t tk = __builtin_amdgcn_readlane(tl, r);
-      const char* src = kseq_b + static_cast<uint64_t>(tk > 0 ? tk : 0) * pitch;
-      dma16(src, (16u * ln) ^ (16u * main_swz(r)), lb + 1024u * r);
+  auto gather_rope = [&](int j, int32_t tl, uint32_t lb, int ln) __attribute__((always_inline)) {
+    const int g8 = N_ROPE * gl + j;   // rows 8 g8 .. 8 g8 + 7
+    const uint32_t rr = 8 * g8 + (ln >> 3);
+    const int32_t t8 = __shfl(tl, static_cast<int>(rr), 64);
+    const uint32_t voff = static_cast<uint32_t>(t8 > 0 ? t8 : 0) * static_cast<uint32_t>(pitch) + 1024u +
+                          16u * ((ln & 7) ^ rope_swz(rr));
+    dma16(kseq_b, voff, lb + KT_MAIN + 1024u * g8);
+  };
+  // load c of a wave's share of one tile: the second group (plan 1) takes
+  // N_MAIN main rows below 16, then N_ROPE rope loads; the first group
+  // (plan 2) N_MAIN main rows from 16
+  auto gather_c = [&](auto plan, int c, int32_t tl, uint32_t lb, int ln) __attribute__((always_inline)) {
+    if constexpr (decltype(plan)::value == 1) {
+      if (c < N_MAIN) gather_main(gl + GW * c, tl, lb, ln);
+      else gather_rope(c - N_MAIN, tl, lb, ln);
     } else {
-      const uint32_t rr = 8 * gl + (ln >> 3);
-      const uint32_t voff = static_cast<uint32_t>(t8 > 0 ? t8 : 0) * static_cast<uint32_t>(pitch) + 1024u +
-                            16u * ((ln & 7) ^ rope_swz(rr));
-      dma16(kseq_b, voff, lb + KT_MAIN + 1024u * gl);
+      gather_main(16 + gl + GW * c, tl, lb, ln);
     }
   };
   auto live_of = [&](int u) __attribute__((always_inline)) -> uint32_t {
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   const uint32_t cr = KT_MAIN + col * 128u + ((32u * q) ^ (16u * rope_swz(col)));
   constexpr int SD = 4;   // K fragments read ahead (products in the order ks, mb)
   // scores of the tile in buffer bs, for key blocks 0 and 1
-  auto scores = [&](auto with_gather, int bs, f32x4_t& s0, f32x4_t& s1, int32_t tl, int32_t t8,
+  auto scores = [&](auto with_gather, int bs, f32x4_t& s0, f32x4_t& s1, int32_t tl,
                     int bg) __attribute__((always_inline)) {
     uint32_t xs = cs, xr = cr;
     int ln = lane;
@@ -328,11 +340,12 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       if (i + SD < 36) kf[i % SD] = frag(i + SD);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // and one LDS read, in turn
-      constexpr int plan = decltype(with_gather)::value;   // 0: none, 1: waves 4..7, 2: waves 0..3
-      if constexpr (plan == 1)
-        if (i % 7 == 6) gather_k(i < 28 ? i / 7 : 8, tl, t8, lb, ln);   // k = 0, 1, 2, 3, the rope
-      if constexpr (plan == 2)
-        if (i % 9 == 8) gather_k(4 + i / 9, tl, t8, lb, ln);            // k = 4..7
+      // the group's loads, spread evenly over the 36 products
+      constexpr int plan = decltype(with_gather)::value;   // 0: none, 1: second group, 2: first group
+      if constexpr (plan != 0) {
+        constexpr int NL = plan == 1 ? N_MAIN + N_ROPE : N_MAIN;
+        if ((i + 1) * NL / 36 != i * NL / 36) gather_c(with_gather, (i + 1) * NL / 36 - 1, tl, lb, ln);
+      }
     }
   };
   // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
@@ -418,16 +431,18 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
 
   // the first two tiles
   __syncthreads();   // token ring filled
-  int32_t g_tl = 0, g_t8 = 0;   // token ids of the next tile to gather
+  int32_t g_tl = 0;   // token ids of the next tile to gather (second group)
   if (grp == 1) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     for (int u = 0; u < 2 && u < n_tiles; ++u) {
-      gather_tokens(u, g_tl, g_t8);
+      g_tl = tokens_of(u);
 #pragma unroll
-      for (int k = 0; k < 9; ++k) gather_k(k, g_tl, g_t8, kb_lds + u * KT_BYTES, ln);
+      for (int k = 0; k < 32 / GW; ++k) gather_main(gl + GW * k, g_tl, kb_lds + u * KT_BYTES, ln);
+#pragma unroll
+      for (int j = 0; j < N_ROPE; ++j) gather_rope(j, g_tl, kb_lds + u * KT_BYTES, ln);
     }
-    if (n_tiles > 2) gather_tokens(2, g_tl, g_t8);
+    if (n_tiles > 2) g_tl = tokens_of(2);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
@@ -437,22 +452,32 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
   // validated and stored in segment 32 j + 3, into the slots of tiles
   // 16 j - 16 .. 16 j - 1, which segment 32 j read last
   const bool token_mode = p.idx != nullptr && p.c == 1;
-  int32_t ring_v = -1;
+  constexpr int RPT = 16 * TILE / (64 * NW);   // refill entries per thread
+  int32_t ring_v[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) ring_v[i] = -1;
   // the part of segment sg that every wave does: its share of the ring refill
   auto segment_io = [&](int sg) __attribute__((always_inline)) {
     const int m = sg >> 1;
     if ((sg & 31) == 1 && sg > 32 && m + 16 < n_tiles) {
-      const int64_t pos = p0 + static_cast<int64_t>(m + 16) * TILE + tid;
-      if (token_mode) ring_v = p.idx[row * p.k_sel + (pos < p1 ? pos : p1 - 1)];
-      else ring_v = pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int64_t pos = p0 + static_cast<int64_t>(m + 16) * TILE + tid + 64 * NW * i;
+        if (token_mode) ring_v[i] = p.idx[row * p.k_sel + (pos < p1 ? pos : p1 - 1)];
+        else ring_v[i] = pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
+      }
     }
     if ((sg & 31) == 3 && sg > 32 && m + 15 < n_tiles) {
       const int base = (m + 15) * TILE;   // m + 15 = 16 j + 16
-      const int64_t pos = p0 + base + tid;
-      int32_t v = ring_v;
-      if (pos >= p1) v = -1;
-      else if (token_mode && !(v >= 0 && v < si.n_vis)) v = -1;
-      s_tok[(base + tid) & (TOK_RING - 1)] = v;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int e = tid + 64 * NW * i;
+        const int64_t pos = p0 + base + e;
+        int32_t v = ring_v[i];
+        if (pos >= p1) v = -1;
+        else if (token_mode && !(v >= 0 && v < si.n_vis)) v = -1;
+        s_tok[(base + e) & (TOK_RING - 1)] = v;
+      }
     }
   };
   auto segment_end = [&](int sg) __attribute__((always_inline)) {
@@ -475,7 +500,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       // at u = 0 this reloads rows of tile 1 with the same bytes, and past
       // the stream it loads rows nothing reads)
       __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
-      scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), 0, (u + 1) % KT_NBUF);
+      scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), (u + 1) % KT_NBUF);
       rescale(softmax(s0, s1, live_of(u), ph, pl));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u);
@@ -496,12 +521,12 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnParams p) {
       f32x4_t s0, s1;
       u32x4_t ph, pl;
       __builtin_amdgcn_s_setprio(2);
-      scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, g_t8, (u + 2) % KT_NBUF);
+      scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, (u + 2) % KT_NBUF);
       rescale(softmax(s0, s1, live_of(u), ph, pl));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u + 1);
       segment_io(2 * u + 2);
-      gather_tokens(u + 3, g_tl, g_t8);   // for the next score segment
+      g_tl = tokens_of(u + 3);   // for the next score segment
       pv(u % KT_NBUF, ph, pl);
       segment_end(2 * u + 2);
     }
