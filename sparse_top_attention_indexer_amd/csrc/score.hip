@@ -314,19 +314,21 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 
 // Prefill variant (n_q a multiple of 4, no histogram): one workgroup = 4
 // consecutive query rows of one sequence (one wave each) x one chunk of
-// 32-key tiles, taken two tiles at a time.  The key tiles are gathered once
-// per workgroup into LDS with direct global -> LDS loads, one tile pair
-// ahead, and read by all four waves; the products of the second tile of a
-// pair are issued before the epilogue of the first.  The scores of the chunk
+// 32-key tiles.  The key tiles are gathered once per workgroup into LDS with
+// direct global -> LDS loads, two tiles ahead (three tile buffers), and read
+// by all four waves.  Three workgroups share a CU (148 registers, 40 KB of
+// LDS), so that three waves per SIMD interleave their products and
+// epilogues; with a rotated or non-bf16 q split into two operands, two
+// workgroups (more registers).  The scores of the chunk
 // collect in LDS and leave in one coalesced pass at the end (so that no store
 // sits between the tile loads in the memory queue).  Tile layout: key row r
 // (256 bytes, 2-byte keys, D = 128) keeps its 16-byte chunk c in slot
 // c ^ (r & 15), so that a wave's B-operand read (lane n: row n, chunk
 // 8 h2 + ks) is free of LDS bank conflicts.
-constexpr int SC_PAIR_BYTES = 2 * 32 * 256;   // two key tiles
-constexpr int SC_NBUF = 3;                      // tile pairs: computing, landed, in flight
+constexpr int SC_TILE_BYTES = 32 * 256;   // one key tile
+constexpr int SC_NBUF = 3;                      // tiles: computing, landed, in flight
 constexpr int SC_MAX_TILES = 32;                // chunk_tiles bound for this kernel
-constexpr size_t SC_LDS = SC_NBUF * SC_PAIR_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
+constexpr size_t SC_LDS = SC_NBUF * SC_TILE_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
 
 typedef __attribute__((address_space(3))) void sc_lds_void_t;
 
@@ -336,12 +338,12 @@ __device__ __forceinline__ void sc_dma16(const void* sbase, uint32_t voff, uint3
 }
 
 template <int KK, int QK, int RB, int NQ>
-__global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
+__global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(ScoreParams p) {
   static_assert(KK == KK_BF16 || KK == KK_F16, "2-byte keys only");
   constexpr bool F16OP = KK == KK_F16;
   extern __shared__ __align__(16) uint8_t s_raw[];
-  uint8_t* s_kt = s_raw;                                                      // SC_NBUF tile pairs
-  float* s_sc = reinterpret_cast<float*>(s_raw + SC_NBUF * SC_PAIR_BYTES);   // [4][chunk_tiles * 32]
+  uint8_t* s_kt = s_raw;                                                      // SC_NBUF tiles
+  float* s_sc = reinterpret_cast<float*>(s_raw + SC_NBUF * SC_TILE_BYTES);   // [4][chunk_tiles * 32]
   int32_t* s_tend = reinterpret_cast<int32_t*>(s_sc + 4 * SC_MAX_TILES * 32);
 
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -373,29 +375,26 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
   if (lane == 0) s_tend[wid] = t_own;
   __syncthreads();
   const int n_t = max(max(s_tend[0], s_tend[1]), max(s_tend[2], s_tend[3]));   // tiles of the workgroup
-  const int n_pairs = (n_t + 1) >> 1;
 
-  // gather of tile pair T into slot T % SC_NBUF: wave w loads rows 8 w .. 8 w + 7
-  // of both tiles (four 1 KB loads; lane L of load i: tile i >> 1, row
-  // 8 w + 4 (i & 1) + L / 16, slot L & 15)
+  // gather of tile T into slot T % SC_NBUF: wave w loads rows 8 w .. 8 w + 7
+  // (two 1 KB loads; lane L of load i: row 8 w + 4 i + L / 16, slot L & 15)
   const uint32_t kt_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((sc_lds_void_t*)s_kt));
   const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * 256;
   auto issue = [&](int T) __attribute__((always_inline)) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int r = 8 * wid + 4 * (i & 1) + (ln >> 4);
-      int64_t u = u_begin + static_cast<int64_t>(2 * T + (i >> 1)) * 32 + r;
+      int64_t u = u_begin + static_cast<int64_t>(T) * 32 + r;
       if (u >= p.n_units) u = p.n_units - 1;   // past the end: any valid row, never used
       const uint32_t voff = static_cast<uint32_t>(u) * 256u + 16u * ((ln & 15) ^ (r & 15));
       sc_dma16(kbase, voff,
-               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_PAIR_BYTES + 8192u * (i >> 1) +
-                                              1024u * (2 * wid + (i & 1))));
+               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_TILE_BYTES + 1024u * (2 * wid + (i & 1))));
     }
   };
-  if (n_pairs > 0) issue(0);
-  if (n_pairs > 1) issue(1);
+  if (n_t > 0) issue(0);
+  if (n_t > 1) issue(1);
 
   u32x4_t qa[RB][8][NQ];
   float wv[RB][16];
@@ -431,21 +430,19 @@ __global__ __launch_bounds__(256, 2) void score_tiled_kernel(ScoreParams p) {
     if (h2 == 0) s_sc[wid * (SC_MAX_TILES * 32) + t * 32 + n] = u < n_vis ? tot : NEG_INF;
   };
 
-  for (int T = 0; T < n_pairs; ++T) {
-    // pair T has landed: only the four loads of pair T + 1 may still be in flight
-    if (T + 1 < n_pairs) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
-    __syncthreads();                                             // for every wave; slot of T - 1 free
-    if (T + 2 < n_pairs) issue(T + 2);
-    if (2 * T < t_own) {
-      const uint8_t* kt = s_kt + (T % SC_NBUF) * SC_PAIR_BYTES + b_off;
+  for (int T = 0; T < n_t; ++T) {
+    // tile T has landed: only the two loads of tile T + 1 may still be in flight
+    if (T + 1 < n_t) __builtin_amdgcn_s_waitcnt(0x0f72);   // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
+    __syncthreads();                                        // for every wave; slot of T - 1 free
+    if (T + 2 < n_t) issue(T + 2);
+    if (T < t_own) {
+      const uint8_t* kt = s_kt + (T % SC_NBUF) * SC_TILE_BYTES + b_off;
       uint32_t hx = 8u * h2;
       asm volatile("" : "+v"(hx));
-      f32x16_t acc0[RB], acc1[RB];
+      f32x16_t acc0[RB];
       products(kt, hx, acc0);
-      products(kt + 8192, hx, acc1);   // the second tile (past t_own: computed, not kept)
-      epilogue(acc0, 2 * T);
-      epilogue(acc1, 2 * T + 1);
+      epilogue(acc0, T);
     }
   }
   // write-out: computed tiles, then -inf for the invisible rest when asked
