@@ -94,8 +94,8 @@ def lib():
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
-            raise DsaError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                           "(there is no fallback implementation)")
+            raise DsaError(f"{LIB_PATH} is missing: build it with "
+                           "sparse_top_attention_indexer_amd.build.build() (there is no fallback implementation)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SYMBOLS.items():
             f = getattr(L, name)
