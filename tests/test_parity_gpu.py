@@ -294,6 +294,39 @@ def test_gqa_token_mode_uneven_groups_split_streams():
         assert np.all(np.abs(got16[s, i] - r) <= 2e-2 * np.maximum(1.0, np.abs(r)))
 
 
+MLA_SHAPE_CASES = {
+    # 48 heads: waves 3..7 of the workgroup hold no heads; decode-like rows
+    # with a split stream
+    "mla_48_heads_split": lambda: inputs.Workload(
+        "mla48", 3, 2, 1500, 1400, 32, 128, torch.bfloat16, torch.bfloat16, "normal", 0.2, 900, 1, 1, False,
+        "mla", 48, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=94),
+    # 144 heads: a second row of workgroups with one wave of heads
+    "mla_144_heads": lambda: inputs.Workload(
+        "mla144", 1, 40, 700, 660, 32, 128, torch.bfloat16, torch.bfloat16, "normal", 0.2, 300, 1, 0, False,
+        "mla", 144, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=95),
+    # block mode: 16-token blocks plus the tail
+    "mla_block_mode": lambda: inputs.Workload(
+        "mlablk", 1, 60, 1000, 940, 16, 128, torch.bfloat16, torch.bfloat16, "normal", 0.25, 256, 16, 0, False,
+        "mla", 128, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=96),
+}
+
+
+@pytest.mark.parametrize("case", list(MLA_SHAPE_CASES))
+def test_mla_head_counts_and_block_mode(case):
+    wl = MLA_SHAPE_CASES[case]()
+    x = inputs.generate(wl)
+    idx, _ = _oracle_idx(x, wl)
+    d = dev(x)
+    got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], torch.from_numpy(idx).to(torch.int32).to(DEV),
+                          c=wl.c, kv_len=d["kv_len"], scale=wl.scale).cpu().double().numpy()
+    rows = _rows_sample(wl, 16, seed=3)
+    ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), idx, x["q_pos"].numpy(),
+                             x["kv_len"].numpy(), wl.c, wl.scale, rows)
+    err = max(float(np.abs(got[s, i] - ref[s, i]).max()) for s, i in rows)
+    print(f"{case}: max |O - oracle| {err:.2e} over {len(rows)} rows")
+    assert err <= 2e-2
+
+
 def test_attention_bf16_output_and_empty_rows():
     wl = inputs.mini(2)
     x = inputs.generate(wl)
