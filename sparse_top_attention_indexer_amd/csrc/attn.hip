@@ -119,6 +119,17 @@ constexpr int KT_NBUF = 3;                       // tiles read by the two wave g
 constexpr int TOK_RING = 1024;                   // validated token ids of 32 tiles
 constexpr size_t MLA_LDS = KT_NBUF * KT_BYTES + TOK_RING * 4 + 64 + MLA_MAX_BLOCKS * 4;
 
+// Softmax weights reach the PV product rounded to bf16 (relative error up to
+// 2^-9).  If the normaliser is summed from the same rounded weights, the
+// output is an exact average under perturbed weights w_j (1 + e_j), and
+// its error is sum_j w_j e_j (v_j - o): independent small terms when the
+// weights are spread, but up to 2^-9 |v_j - o| when one weight dominates
+// (x8 outlier rows: several 1e-2).  So a tile whose largest weight in some
+// head of the wave exceeds LO_SHARE of that head's normaliser so far also
+// runs the bf16 residual of its weights (exact to ~2^-17); every other tile
+// uses the high part alone, and every later weight only shrinks its share.
+constexpr float LO_SHARE = 1.f / 16.f;
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -171,8 +182,9 @@ __device__ __forceinline__ float quad_sum(float x) {
 //       blocks), K fragments read from the LDS tile, Q in registers
 //   online softmax over the 32 keys of each head (8 per lane + two lane
 //       swaps); the running max is only raised when it grows by more than 2^8
-//       in weight, and the weights enter the PV product as a bf16 high part
-//       plus a bf16 residual, so they stay exact to ~2^-17 even above 1
+//       in weight.  The weights enter the PV product as a bf16 high part,
+//       plus a bf16 residual when some weight of the tile is large against
+//       the running normaliser (see LO_SHARE)
 //   O^T (512 dims x 16 heads) += V^T . P^T: V^T fragments come straight from
 //       the key-major tile through the transposing LDS read; P^T is the S^T
 //       accumulator layout, so no data moves between lanes
@@ -351,7 +363,8 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
   // P^T fragments (k slot j < 4: key 4 q + j; j >= 4: key 16 + 4 q + j - 4)
   // and returns the factor that rescales what was accumulated before.
-  auto softmax = [&](f32x4_t s0, f32x4_t s1, uint32_t live, u32x4_t& ph, u32x4_t& pl) __attribute__((always_inline)) -> float {
+  auto softmax = [&](f32x4_t s0, f32x4_t s1, uint32_t live, u32x4_t& ph, u32x4_t& pl,
+                     bool& need_lo) __attribute__((always_inline)) -> float {
     if (live != 0xffffffffu) {
       const uint32_t lm = live >> (4 * q);
 #pragma unroll
@@ -375,16 +388,21 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb));
     }
     uint32_t hv[4], lv[4];
-    float psum = 0.f;
+    float psum = 0.f, hsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-      lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
+      const float h0 = __uint_as_float(hv[i] << 16), h1 = __uint_as_float(hv[i] & 0xffff0000u);
+      lv[i] = pack_bf16x2(x[2 * i] - h0, x[2 * i + 1] - h1);
       psum += x[2 * i] + x[2 * i + 1];
+      hsum += h0 + h1;
     }
     ph = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
     pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
-    l_run = l_run * alpha + quad_sum(psum);
+    const float la = l_run * alpha, l_full = la + quad_sum(psum);
+    const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));   // the head's largest weight in the tile
+    need_lo = __ballot(xmax > LO_SHARE * l_full) != 0;   // wave-uniform
+    l_run = need_lo ? l_full : la + quad_sum(hsum);
     return alpha;
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
@@ -404,7 +422,9 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     cv = R * 1024 + 16 * ((r4 >> 1) ^ (f & 1)) + 16 * (f & 14) + 8 * (r4 & 1);
   }
   constexpr int VD = 3;   // V^T fragments read ahead
-  auto pv = [&](int bp, const u32x4_t& ph, const u32x4_t& pl) __attribute__((always_inline)) {
+  // one pass of O^T += V^T . P^T over the 32 dim blocks, P^T = the weights'
+  // high part or (a second pass over the same tile) their residual
+  auto pv = [&](int bp, const u32x4_t& pw) __attribute__((always_inline)) {
     uint32_t x1 = cv;
     asm volatile("" : "+v"(x1));
     uint8_t* kt = s_kb + bp * KT_BYTES;
@@ -421,10 +441,9 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * VD, 0);
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
-      o[db] = mfma16x16x32_bf16(vf[db % VD], ph, o[db]);
-      o[db] = mfma16x16x32_bf16(vf[db % VD], pl, o[db]);
+      o[db] = mfma16x16x32_bf16(vf[db % VD], pw, o[db]);
       if (db + VD < 32) vf[db % VD] = vfrag(db + VD);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
@@ -496,16 +515,22 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       segment_io(2 * u);
       f32x4_t s0, s1;
       u32x4_t ph, pl;
+      bool need_lo;
       // tile u + 1 past tile 1 (the first two come whole from the prologue;
       // at u = 0 this reloads rows of tile 1 with the same bytes, and past
       // the stream it loads rows nothing reads)
       __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
       scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), (u + 1) % KT_NBUF);
-      rescale(softmax(s0, s1, live_of(u), ph, pl));
+      rescale(softmax(s0, s1, live_of(u), ph, pl, need_lo));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u);
       segment_io(2 * u + 1);
-      pv(u % KT_NBUF, ph, pl);
+      u32x4_t pw = ph;
+#pragma clang loop unroll(disable)
+      for (int ps = 0; ps < 1 + need_lo; ++ps) {
+        pv(u % KT_NBUF, pw);
+        pw = pl;
+      }
       segment_end(2 * u + 1);
     }
     segment_io(2 * n_tiles);
@@ -520,14 +545,20 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       segment_io(2 * u + 1);
       f32x4_t s0, s1;
       u32x4_t ph, pl;
+      bool need_lo;
       __builtin_amdgcn_s_setprio(2);
       scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, (u + 2) % KT_NBUF);
-      rescale(softmax(s0, s1, live_of(u), ph, pl));
+      rescale(softmax(s0, s1, live_of(u), ph, pl, need_lo));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u + 1);
       segment_io(2 * u + 2);
       g_tl = tokens_of(u + 3);   // for the next score segment
-      pv(u % KT_NBUF, ph, pl);
+      u32x4_t pw = ph;
+#pragma clang loop unroll(disable)
+      for (int ps = 0; ps < 1 + need_lo; ++ps) {
+        pv(u % KT_NBUF, pw);
+        pw = pl;
+      }
       segment_end(2 * u + 2);
     }
   }
