@@ -28,7 +28,13 @@ and notation of the pages:
     indexer is an exact no-op when top_k >= n_tokens);
   * the orthonormal Sylvester Walsh-Hadamard rotation of indexer q and k
     ((Hq).(Hk) = q.k, H symmetric with H.H = I: PR #2058 first and
-    "kr_l maintenance" commits).
+    "kr_l maintenance" commits);
+  * the indexer-key cache write: new keys rotated in float32 and stored in the
+    cache type (f16, bf16, or fp8 e4m3fn with a per-row scale) at their cache
+    rows (PR #2058 "decode-correct indexer-K cache" commit; quantized indexer
+    and K caches in the ik_llama_opt log and the deepseek41 PR).  This part
+    alone runs in float32, because its stored codes are integers that a
+    float decides (see its section).
 
 Where the pages leave a step open, the reading taken is stated at the function
 that takes it.  Every function is pinned by tests in tests/test_oracle.py
@@ -396,3 +402,100 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
     idx = topk(scores, q_pos, top_k // c, kv_len, c, n_sink, rows)
     O = sparse_attention(Q, K, V, idx, q_pos, kv_len, c, scale, rows)
     return O, idx, scores
+
+
+# --------------------------------------------------------------------------
+# Indexer-key cache write: rotate, then store in the cache type.
+# --------------------------------------------------------------------------
+#
+# ik_llama.cpp PR #2058, "decode-correct indexer-K cache" commit: the batch's
+# Walsh-Hadamard-rotated indexer keys are written into the per-layer key cache
+# at kv_head, and later read back whole for scoring; ik_llama_opt log,
+# "GLM-DSA: allow for quantized indexer cache"; ik_llama.cpp PR "deepseek41
+# quantized K cache": rows are rotated in F32 and then stored in the cache
+# type.  The cache types here are f16, bf16 and fp8 e4m3fn with one f32 scale
+# per row (the long-decode workload's format; not on the pages).
+#
+# Because a stored code is an integer decided by floating point, this part
+# computes in float32, the precision the pages name for the rotation, instead
+# of float64: the rotation is the fast Walsh-Hadamard transform (butterfly
+# spans 1, 2, 4, ..., 64, in that order, (a, b) -> (a + b, a - b)), then a
+# multiplication by float32(1/sqrt(128)); every step is one correctly rounded
+# float32 operation, so the result is fixed bit for bit.
+
+FP8_E4M3_MAX = 448.0
+
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Normalised Walsh-Hadamard transform of the last axis in float32.
+
+    Equals hadamard(n) @ x up to float32 rounding; the butterfly order above
+    fixes the rounding.  The last axis must be a power of two.
+    """
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    if n < 1 or n & (n - 1):
+        raise ValueError("transform length must be a power of two")
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        # last axis as (block, half, offset): element blk*2h + half*h + r
+        y = y.reshape(lead + (n // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        y = y.reshape(lead + (n,))
+        h *= 2
+    return y * np.float32(1.0 / math.sqrt(n))
+
+
+def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """float32 values -> OCP e4m3fn codes (uint8).
+
+    The nearest finite e4m3fn value, ties to the even code (the code's last
+    bit is the mantissa's last bit); magnitudes above 448 saturate to 448; the
+    sign bit is kept (so -0.0 and negative values that round to zero give
+    0x80).  Written from the format's definition: the magnitude is compared
+    with the table of the 127 non-negative finite values.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    table = decode_fp8_e4m3fn(np.arange(127, dtype=np.uint8))   # codes 0..126, ascending values
+    a = np.abs(v).astype(np.float64)
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a >= FP8_E4M3_MAX, 126, code)
+    sign = np.signbit(v).astype(np.int64)
+    return (code | (sign << 7)).astype(np.uint8)
+
+
+def index_key_write(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool):
+    """Rows to store for new indexer keys [..., D] (exact float32 values).
+
+    cache_dtype 'f16' or 'bf16': returns the rounded (nearest, ties to even)
+    uint16 bit patterns, and None.  'fp8': returns (codes uint8 [..., D],
+    scale float32 [...]) with scale = amax / 448 of the (rotated) row and code
+    = e4m3fn(k / scale), both in float32; a row of zeros gets scale 0 and
+    codes 0.  hadamard_k rotates the row first (D must be 128).
+    """
+    x = np.asarray(k_new, dtype=np.float32)
+    if hadamard_k:
+        if x.shape[-1] != 128:
+            raise ValueError("the rotation is defined for 128-wide keys")
+        x = fwht_f32(x)
+    if cache_dtype == "f16":
+        return x.astype(np.float16).view(np.uint16), None
+    if cache_dtype == "bf16":
+        import torch  # the library's float32 -> bfloat16 rounding (nearest, ties to even)
+
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), None
+    if cache_dtype != "fp8":
+        raise ValueError(cache_dtype)
+    amax = np.abs(x).max(axis=-1).astype(np.float32)
+    scale = (amax / np.float32(FP8_E4M3_MAX)).astype(np.float32)
+    q = np.zeros_like(x)
+    np.divide(x, scale[..., None], out=q, where=scale[..., None] > 0)
+    return encode_fp8_e4m3fn(q.astype(np.float32)), scale

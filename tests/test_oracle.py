@@ -389,3 +389,88 @@ def test_attention_token_order_only_changes_rounding():
     a = O.sparse_attention(Q, K, V, np.array([[[3, 9, 17, 30, 31]]]), np.array([[39]]))
     b = O.sparse_attention(Q, K, V, np.array([[[31, 17, 3, 30, 9]]]), np.array([[39]]))
     assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------ indexer-key cache write --
+
+def test_fwht_f32_matches_the_hadamard_matrix():
+    # the fast butterflies compute the Sylvester matrix product (fp64 reference)
+    x = np.random.default_rng(11).standard_normal((64, 128)).astype(np.float32)
+    ref = x.astype(np.float64) @ O.hadamard(128)
+    got = O.fwht_f32(x)
+    assert got.dtype == np.float32
+    assert np.abs(got - ref).max() <= 1e-6 * np.abs(x).max() * math.sqrt(128)
+
+
+def test_fwht_f32_of_basis_vectors_is_exact():
+    # H e_j is column j of H: entries +-1/sqrt(128), exact after the float32 scaling
+    eye = np.eye(128, dtype=np.float32)
+    got = O.fwht_f32(eye)
+    c = np.float32(1.0 / math.sqrt(128.0))
+    sign = np.sign(O.hadamard(128) * math.sqrt(128)).astype(np.float32)
+    assert np.array_equal(got, sign * c)
+
+
+def test_fwht_f32_twice_is_identity():
+    # H is symmetric and orthonormal: H.H = I (pages: un-rotation is a second rotation)
+    x = np.random.default_rng(12).standard_normal((16, 128)).astype(np.float32)
+    assert np.abs(O.fwht_f32(O.fwht_f32(x)) - x).max() < 1e-5
+
+
+def test_fp8_encode_matches_torch_in_range():
+    # torch's float32 -> float8_e4m3fn cast (round to nearest even) for finite in-range values,
+    # including every exact midpoint between neighbouring codes and the subnormal range
+    g = np.random.default_rng(13)
+    vals = [g.uniform(-448, 448, 20000), g.standard_normal(20000) * 1e-2, g.uniform(-2**-6, 2**-6, 5000)]
+    table = O.decode_fp8_e4m3fn(np.arange(127, dtype=np.uint8))
+    mids = (table[:-1] + table[1:]) / 2
+    vals += [mids, -mids, table, -table, [0.0, -0.0]]
+    v = np.concatenate([np.asarray(a, dtype=np.float64) for a in vals]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_fp8_e4m3fn(v), ref)
+
+
+def test_fp8_encode_round_trip_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.encode_fp8_e4m3fn(O.decode_fp8_e4m3fn(codes).astype(np.float32)), codes)
+    big = np.array([448.0, 449.0, 463.9, 464.0, 1e6, -500.0], dtype=np.float32)
+    assert list(O.encode_fp8_e4m3fn(big)) == [0x7E] * 5 + [0xFE]
+    # ties go to the even code: 0.5 * (1 + 1.125) lies halfway between codes 0x38 and 0x39
+    assert O.encode_fp8_e4m3fn(np.float32(1.0625))[()] == 0x38
+    assert O.encode_fp8_e4m3fn(np.float32(1.1875))[()] == 0x3A   # between 0x39 and 0x3A: even wins
+
+
+def test_key_write_fp8_bounds_and_extremes():
+    g = np.random.default_rng(14)
+    k = g.standard_normal((40, 128)).astype(np.float32)
+    k[3] *= 8.0
+    k[5] = 0.0
+    for rot in (False, True):
+        codes, scale = O.index_key_write(k, "fp8", rot)
+        x = O.fwht_f32(k) if rot else k
+        assert scale.dtype == np.float32 and codes.dtype == np.uint8
+        assert scale[5] == 0 and not codes[5].any()
+        live = np.arange(40) != 5
+        # the largest magnitude of each row is stored as +-448
+        arg = np.abs(x[live]).argmax(-1)
+        assert np.all((codes[live][np.arange(39), arg] & 0x7F) == 0x7E)
+        # half-ulp bound of 3 mantissa bits (absolute 2^-10 in the subnormal range), in scale units
+        dec = O.decode_fp8_e4m3fn(codes) * scale[:, None].astype(np.float64)
+        q = x.astype(np.float64) / np.where(scale > 0, scale, 1)[:, None]
+        bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) * scale[:, None] * (1 + 1e-6)
+        assert np.all(np.abs(dec - x) <= bound)
+
+
+def test_key_write_16bit_rows_and_rotation_invariance():
+    g = np.random.default_rng(15)
+    k = g.standard_normal((8, 128)).astype(np.float32)
+    q = g.standard_normal((3, 128))
+    bits16, none = O.index_key_write(k, "f16", True)
+    assert none is None
+    assert np.array_equal(bits16, O.fwht_f32(k).astype(np.float16).view(np.uint16))
+    # scoring rotated q against the stored rotated keys recovers q . k (f16 storage precision)
+    stored = O.decode_f16(bits16)
+    d_rot = (q @ O.hadamard(128)) @ stored.T
+    assert np.abs(d_rot - q @ k.T.astype(np.float64)).max() < 2e-2
+    bb, _ = O.index_key_write(k, "bf16", False)
+    assert np.abs(O.decode_bf16(bb) - k).max() <= 2.0 ** -8 * np.abs(k).max()
