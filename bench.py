@@ -7,7 +7,10 @@ line.  The default workload is the 4096-token DSA prefill (128-head MLA
 attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1..5]
-                    [--no-cpu-baseline] [--calib-copy]
+                    [--no-cpu-baseline] [--no-next-rows] [--calib-copy]
+
+Beside the hot path it times the indexer-key cache write (rotate + fp8
+quantise) at the long-decode cache shape, reported under "next_rows".
 """
 
 import argparse
@@ -35,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: DSA prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the rows measured beside the hot path (the indexer-key cache write)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (counter calibration)")
@@ -176,6 +181,39 @@ def cpu_baseline(wl, x, budget_s):
                       f"(evenly spread), numpy float64 oracle, {t_total:.1f} s"}
 
 
+# ------------------------------------------------ next row: key cache write
+
+def key_write_row(dsa, inputs, torch, steps):
+    """The indexer-key cache write at the long-decode cache shape: 8 x 131072
+    new bf16 keys rotated and stored as fp8 e4m3fn + f32 row scales in one
+    call.  Timed with HIP events on the stream the binding launches on; HBM
+    roofline on algorithmic bytes (each key row read once, its codes and
+    scale written once)."""
+    S, n = 8, 131072
+    b = inputs.key_write_batch(S, n, n, torch.bfloat16, seed=2005, skipped=0, device="cuda")
+    cache = torch.empty((S, n, 128), dtype=torch.float8_e4m3fn, device="cuda")
+    scale = torch.empty((S, n), dtype=torch.float32, device="cuda")
+
+    def run():
+        dsa.index_key_write(b["k_new"], cache, cache_scale=scale, hadamard=True)
+
+    for _ in range(3):
+        run()
+    ev = [dsa.Event() for _ in range(steps + 1)]
+    ev[0].record()
+    for k in range(steps):
+        run()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[k].elapsed_ms(ev[k + 1]) for k in range(steps)) / steps
+    per_row = 128 * 2 + 128 + 4
+    by = S * n * per_row
+    return {"workload": "index_key_write_8x131072_bf16_to_fp8_rotated", "kernel": "key_write_kernel",
+            "ms": round(ms, 5), "rows_per_s": S * n / (ms * 1e-3), "bytes_per_row": per_row,
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": by / (ms * 1e-3) / PEAK_HBM}}
+
+
 # ---------------------------------------------------------------------- main
 
 def main():
@@ -267,6 +305,8 @@ def main():
         "phase_roofline_frac": {k_: round(v_["frac"], 4) for k_, v_ in per_phase.items()},
         "roofline": roof,
     }
+    if not args.no_next_rows:
+        line["next_rows"] = {"index_key_write": key_write_row(dsa, inputs, torch, 20)}
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

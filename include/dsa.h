@@ -26,6 +26,9 @@
  *  - [GATHER]  same log, openPangu port, "Gather OpenPangu DSA decode reads"
  *              and the prefill gather commits: attention over the gathered
  *              selected latent rows, values taken from the same rows.
+ *  - [QKC]     same log, "GLM-DSA: allow for quantized indexer cache", and the
+ *              ik_llama.cpp deepseek41 quantized-K-cache PR: cached rows are
+ *              rotated in F32 before they are stored in the cache type.
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers, row-major, last dimension
@@ -154,6 +157,41 @@ int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx,
 int dsa_block_pool(const void* k_raw, int32_t dtype /* F32 | BF16 | F16 */,
                    int32_t S, int64_t n_kv, int32_t D, int32_t c,
                    float* pooled /* [S, n_kv / c, D] */, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Indexer-key cache write: rotate new keys, store them in the cache type
+ *   [PR2058] decode-correct indexer-K cache commit (rotated keys written at
+ *   the batch's cache rows); [QKC] quantized indexer / K caches (rows rotated
+ *   in F32, then stored in the cache type)
+ *
+ * For new key t of sequence s, with destination row r = dst_row[s, t]
+ * (dst_row == NULL: r = t), when 0 <= r < n_cache (other rows are skipped):
+ *   x = k_new[s, t, :] in f32;  y = sqrt(128) H x when hadamard != 0 (H
+ *       the orthonormal 128-point Sylvester Walsh-Hadamard matrix), else x
+ *   F16 / BF16 cache: cache[s, r, :] = H x (or x) rounded to nearest, ties
+ *       to even
+ *   FP8 cache: with m = max_d |y(d)|, cache[s, r, d] = e4m3fn(y(d) * (448 /
+ *       m)), nearest, ties to the even code, saturating at 448, and
+ *       cache_scale[s, r] = m / (448 sqrt(128)) (m / 448 unrotated), so that
+ *       code * scale = H x to fp8 precision; a zero row stores scale 0 and
+ *       zero codes
+ * Bit-exact definition in f32: y is the fast transform with butterfly spans
+ * 1, 2, 4, ..., 64 in that order ((a, b) -> (a + b, a - b)); H x = y *
+ * f32(1/sqrt(128)); 448 / m is a correctly rounded division; the scale is m
+ * times f32(1/(448 sqrt(128))) (f32(1/448) unrotated).  The stored rows are
+ * what dsa_index_scores reads as keys (hadamard_q = 1 when rotated, k_scale =
+ * cache_scale for fp8).
+ * k_new [S, n_new, D] of k_dtype (F32 | BF16 | F16); cache [S, n_cache, D] of
+ * cache_dtype (F16 | BF16 | FP8_E4M3); cache_scale [S, n_cache] f32 iff FP8
+ * (else NULL); dst_row [S, n_new] int32 device or NULL.  D must be 128 and
+ * S at most 65535;
+ * n_new may be 0 (nothing is written; k_new may then be NULL).  Two new keys with the same
+ * destination row race: one of them is stored.  Non-finite keys store
+ * unspecified codes.
+ * ---------------------------------------------------------------------- */
+int dsa_index_key_write(const void* k_new, int32_t k_dtype, int32_t S, int64_t n_new, int32_t D,
+                        const int32_t* dst_row, int32_t hadamard, void* cache, int32_t cache_dtype,
+                        float* cache_scale, int64_t n_cache, void* stream);
 
 /* ------------------------------------------------------------------------
  * S4 + S5 (+ S6): sparse attention over the selected tokens   [GATHER], [PR2058]

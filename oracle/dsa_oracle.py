@@ -419,9 +419,16 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
 # Because a stored code is an integer decided by floating point, this part
 # computes in float32, the precision the pages name for the rotation, instead
 # of float64: the rotation is the fast Walsh-Hadamard transform (butterfly
-# spans 1, 2, 4, ..., 64, in that order, (a, b) -> (a + b, a - b)), then a
-# multiplication by float32(1/sqrt(128)); every step is one correctly rounded
-# float32 operation, so the result is fixed bit for bit.
+# spans 1, 2, 4, ..., 64, in that order, (a, b) -> (a + b, a - b)), then, for
+# 16-bit caches, a multiplication by float32(1/sqrt(128)); every step is one
+# correctly rounded float32 operation, so the result is fixed bit for bit.
+#
+# fp8 rows (this build's format; the pages fix only that rows are rotated in
+# F32 before they are stored in the cache type): with y the row after the butterflies (not yet
+# normalised) and m = max |y|, code = e4m3fn(y * (448 / m)) and scale =
+# m * float32(1 / (448 sqrt(128))) (1 / 448 for an unrotated row), so that
+# code * scale is the normalised rotated value to within the fp8 rounding.
+# One division per row, none per element.
 
 FP8_E4M3_MAX = 448.0
 
@@ -432,6 +439,13 @@ def fwht_f32(x: np.ndarray) -> np.ndarray:
     Equals hadamard(n) @ x up to float32 rounding; the butterfly order above
     fixes the rounding.  The last axis must be a power of two.
     """
+    y = butterflies_f32(x)
+    return y * np.float32(1.0 / math.sqrt(y.shape[-1]))
+
+
+def butterflies_f32(x: np.ndarray) -> np.ndarray:
+    """The unnormalised fast Walsh-Hadamard transform of the last axis in
+    float32: sqrt(n) * hadamard(n) @ x up to float32 rounding."""
     y = np.array(x, dtype=np.float32, copy=True)
     n = y.shape[-1]
     if n < 1 or n & (n - 1):
@@ -447,7 +461,7 @@ def fwht_f32(x: np.ndarray) -> np.ndarray:
         y[..., 1, :] = a - b
         y = y.reshape(lead + (n,))
         h *= 2
-    return y * np.float32(1.0 / math.sqrt(n))
+    return y
 
 
 def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
@@ -475,27 +489,31 @@ def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
 def index_key_write(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool):
     """Rows to store for new indexer keys [..., D] (exact float32 values).
 
-    cache_dtype 'f16' or 'bf16': returns the rounded (nearest, ties to even)
-    uint16 bit patterns, and None.  'fp8': returns (codes uint8 [..., D],
-    scale float32 [...]) with scale = amax / 448 of the (rotated) row and code
-    = e4m3fn(k / scale), both in float32; a row of zeros gets scale 0 and
-    codes 0.  hadamard_k rotates the row first (D must be 128).
+    cache_dtype 'f16' or 'bf16': returns the rotated (hadamard_k) or plain rows
+    rounded to nearest, ties to even, as uint16 bit patterns, and None.
+    'fp8': returns (codes uint8 [..., D], scale float32 [...]) as described
+    above the section; a row of zeros gets scale 0 and codes 0.  The rotation
+    needs D = 128.
     """
     x = np.asarray(k_new, dtype=np.float32)
-    if hadamard_k:
-        if x.shape[-1] != 128:
-            raise ValueError("the rotation is defined for 128-wide keys")
-        x = fwht_f32(x)
-    if cache_dtype == "f16":
-        return x.astype(np.float16).view(np.uint16), None
-    if cache_dtype == "bf16":
+    if hadamard_k and x.shape[-1] != 128:
+        raise ValueError("the rotation is defined for 128-wide keys")
+    if cache_dtype in ("f16", "bf16"):
+        if hadamard_k:
+            x = fwht_f32(x)
+        if cache_dtype == "f16":
+            return x.astype(np.float16).view(np.uint16), None
         import torch  # the library's float32 -> bfloat16 rounding (nearest, ties to even)
 
         return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), None
     if cache_dtype != "fp8":
         raise ValueError(cache_dtype)
-    amax = np.abs(x).max(axis=-1).astype(np.float32)
-    scale = (amax / np.float32(FP8_E4M3_MAX)).astype(np.float32)
-    q = np.zeros_like(x)
-    np.divide(x, scale[..., None], out=q, where=scale[..., None] > 0)
-    return encode_fp8_e4m3fn(q.astype(np.float32)), scale
+    y = butterflies_f32(x) if hadamard_k else x
+    m = np.abs(y).max(axis=-1).astype(np.float32)
+    live = m > 0
+    inv = np.zeros_like(m)
+    np.divide(np.float32(FP8_E4M3_MAX), m, out=inv, where=live)
+    unit = np.float32(1.0 / (FP8_E4M3_MAX * math.sqrt(128.0))) if hadamard_k else np.float32(1.0 / FP8_E4M3_MAX)
+    scale = (m * unit).astype(np.float32)
+    q = (y * inv[..., None]).astype(np.float32)
+    return encode_fp8_e4m3fn(q), scale

@@ -76,6 +76,7 @@ SYMBOLS = {
     "dsa_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(TopkDesc)]),
     "dsa_topk": (ctypes.c_int, [_vp, ctypes.POINTER(TopkDesc), _vp, _vp, ctypes.c_size_t, _vp]),
     "dsa_block_pool": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "dsa_index_key_write": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _i64, _vp]),
     "dsa_sparse_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc), ctypes.c_int]),
     "dsa_sparse_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "dsa_forward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ForwardDesc)]),
@@ -187,6 +188,29 @@ def block_pool(k_raw, c: int, out=None):
         out = torch.empty((S, n_kv // c, D), device=k_raw.device, dtype=torch.float32)
     _check(lib().dsa_block_pool(_ptr(k_raw.contiguous()), _dt(k_raw), S, n_kv, D, c, _ptr(out), _stream()))
     return out
+
+
+# ------------------------------------------------------ indexer-key cache --
+
+def index_key_write(k_new, cache, *, dst_row=None, cache_scale=None, hadamard: bool = False):
+    """Rotates (hadamard=True) and stores new indexer keys [S, n_new, 128] in
+    the cache [S, n_cache, 128] (f16, bf16 or float8_e4m3fn with cache_scale
+    [S, n_cache] f32) at rows dst_row [S, n_new] int32 (None: rows 0 ..
+    n_new - 1); rows outside the cache are skipped (dsa_index_key_write)."""
+    _need_gpu(k_new, cache, cache_scale, dst_row)
+    if not cache.is_contiguous() or (cache_scale is not None and not cache_scale.is_contiguous()):
+        raise DsaError("the key cache and its scales must be contiguous")
+    S, n_new, D = k_new.shape
+    if cache.dim() != 3 or cache.shape[0] != S or cache.shape[2] != D:
+        raise DsaError("cache must be [S, n_cache, D] with the keys' S and D")
+    if cache_scale is not None and tuple(cache_scale.shape) != tuple(cache.shape[:2]):
+        raise DsaError("cache_scale must be [S, n_cache]")
+    if dst_row is not None and tuple(dst_row.shape) != (S, n_new):
+        raise DsaError("dst_row must be [S, n_new]")
+    _check(lib().dsa_index_key_write(_ptr(k_new.contiguous()), _dt(k_new), S, n_new, D, _ptr(_i32c(dst_row)),
+                                     int(hadamard), _ptr(cache), _dt(cache), _ptr(cache_scale), cache.shape[1],
+                                     _stream()))
+    return cache
 
 
 # --------------------------------------------------------------- attention --

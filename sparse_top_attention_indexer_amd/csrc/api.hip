@@ -229,6 +229,21 @@ int dsa_block_pool(const void* k_raw, int32_t dtype, int32_t S, int64_t n_kv, in
   return hip_status(launch_block_pool(k_raw, dtype, S, n_kv, D, c, pooled, as_stream(stream)));
 }
 
+int dsa_index_key_write(const void* k_new, int32_t k_dtype, int32_t S, int64_t n_new, int32_t D,
+                        const int32_t* dst_row, int32_t hadamard, void* cache, int32_t cache_dtype,
+                        float* cache_scale, int64_t n_cache, void* stream) {
+  if (!cache || (!k_new && n_new != 0)) return DSA_ERR_NULL;   // an empty batch may pass no key buffer
+  if (k_dtype != DSA_F32 && k_dtype != DSA_BF16 && k_dtype != DSA_F16) return DSA_ERR_DTYPE;
+  if (cache_dtype != DSA_BF16 && cache_dtype != DSA_F16 && cache_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  if ((cache_dtype == DSA_FP8_E4M3) != (cache_scale != nullptr)) return cache_scale ? DSA_ERR_PARAM : DSA_ERR_NULL;
+  if (S < 1 || S > 65535 || n_new < 0 || n_cache < 1 || D != 128) return DSA_ERR_SHAPE;
+  if ((n_new + 15) / 16 > 0x7fffffffLL) return DSA_ERR_SHAPE;
+  if (hadamard != 0 && hadamard != 1) return DSA_ERR_PARAM;
+  if (!aligned16(k_new) || !aligned16(cache) || !aligned16(cache_scale) || !aligned16(dst_row)) return DSA_ERR_ALIGN;
+  return hip_status(launch_key_write(k_new, k_dtype, S, n_new, dst_row, hadamard, cache, cache_dtype, cache_scale,
+                                     n_cache, as_stream(stream)));
+}
+
 size_t dsa_sparse_attn_workspace_bytes(const dsa_attn_desc* d, int dense) {
   if (!d || attn_family(d) < 0 || d->S < 1 || d->n_q < 1 || d->n_kv < 1 || d->c < 1) return 0;
   if (!dense && d->k_sel < 1) return 0;

@@ -73,6 +73,10 @@ hipError_t launch_topk_clear(const TopkParams& p, hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st);
 
 // -------------------------------------------------------------- block pool --
+// Indexer-key cache write (rotate, then store as f16 / bf16 / fp8 + row scale).
+hipError_t launch_key_write(const void* k_new, int k_dtype, int S, int64_t n_new, const int32_t* dst_row,
+                            int hadamard, void* cache, int cache_dtype, float* cache_scale, int64_t n_cache,
+                            hipStream_t st);
 hipError_t launch_block_pool(const void* k_raw, int dtype, int S, int64_t n_kv, int D, int c,
                              float* pooled, hipStream_t st);
 

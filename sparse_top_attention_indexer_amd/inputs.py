@@ -184,3 +184,36 @@ def generate(wl: Workload, device="cpu", seed: Optional[int] = None) -> dict:
         out["V"] = (_randn(g, (S, n_kv, wl.Hkv, wl.Dv), device) *
                     row_gain[..., None, None]).to(wl.a_dtype)
     return out
+
+
+def key_write_batch(S: int, n_new: int, n_cache: int, k_dtype=torch.bfloat16, seed: int = 2000,
+                    outlier_frac: float = 0.01, zero_rows: int = 1, skipped: int = 2,
+                    device="cpu") -> dict:
+    """New raw indexer keys for the cache-write step and where they go.
+
+    k_new [S, n_new, 128] ~ N(0,1) in k_dtype, with a seeded share of rows x 8
+    (the long-decode workload's outliers) and `zero_rows` all-zero rows per
+    sequence.  dst_row [S, n_new] int32: distinct cache rows drawn at random
+    per sequence, except that `skipped` entries per sequence point outside the
+    cache (-1, n_cache) and must leave it untouched.  Needs n_new <= n_cache.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    k = torch.randn((S, n_new, 128), generator=g)
+    out = torch.rand((S, n_new), generator=g) < outlier_frac
+    k[out] *= 8.0
+    for s in range(S):
+        k[s, :min(zero_rows, n_new)] = 0.0
+    dst = torch.stack([torch.randperm(n_cache, generator=g)[:n_new] for _ in range(S)]).to(torch.int32)
+    for s in range(S):
+        for j in range(min(skipped, n_new)):
+            dst[s, n_new - 1 - j] = -1 if j % 2 == 0 else n_cache
+    return {"k_new": k.to(k_dtype).to(device), "dst_row": dst.to(device)}
+
+
+def indexer_queries(S: int, n_q: int, H: int = 64, seed: int = 2007) -> dict:
+    """Indexer queries [S, n_q, H, 128] bf16 ~ N(0,1) and head weights
+    [S, n_q, H] f32 ~ N(0,1)/sqrt(H), for scoring a written key cache."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((S, n_q, H, 128), generator=g).to(torch.bfloat16)
+    w = torch.randn((S, n_q, H), generator=g) / math.sqrt(H)
+    return {"q_idx": q, "w": w}

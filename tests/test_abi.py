@@ -182,3 +182,21 @@ def test_forward_workspace_covers_intermediates():
     assert need >= 4096 * 4096 * 4 + 4096 * 2048 * 4   # scores + idx
     assert L.dsa_forward(ctypes.byref(prefill), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
     assert L.dsa_forward(ctypes.byref(prefill), None, need, None) == WORKSPACE
+
+
+@no_gpu
+def test_index_key_write_rejects():
+    L = dsa.lib()
+    f = ctypes.c_void_p(FAKE)
+
+    def call(k=f, kd=1, S=2, n=10, D=128, dst=None, had=1, cache=f, cd=3, sc=f, nc=100):
+        return L.dsa_index_key_write(k, kd, S, n, D, dst, had, cache, cd, sc, nc, None)
+
+    assert call(k=None) == NULL and call(cache=None) == NULL
+    assert call(cd=3, sc=None) == NULL                 # fp8 cache needs its scales
+    assert call(cd=2, sc=f) == PARAM                   # scales without an fp8 cache
+    assert call(kd=3) == DTYPE and call(cd=0, sc=None) == DTYPE and call(cd=9) == DTYPE
+    assert call(S=0) == SHAPE and call(S=65536) == SHAPE and call(n=-1) == SHAPE and call(nc=0) == SHAPE and call(D=64) == SHAPE
+    assert call(had=2) == PARAM
+    assert call(k=ctypes.c_void_p(FAKE + 8)) == ALIGN and call(dst=ctypes.c_void_p(FAKE + 4)) == ALIGN
+    assert call(n=0) == OK and call(k=None, n=0) == OK   # nothing to write: no launch

@@ -411,6 +411,11 @@ def test_fwht_f32_of_basis_vectors_is_exact():
     assert np.array_equal(got, sign * c)
 
 
+def test_butterflies_are_the_unnormalised_transform():
+    x = np.random.default_rng(16).standard_normal((8, 128)).astype(np.float32)
+    assert np.abs(O.butterflies_f32(x) - math.sqrt(128) * (x.astype(np.float64) @ O.hadamard(128))).max() < 1e-4
+
+
 def test_fwht_f32_twice_is_identity():
     # H is symmetric and orthonormal: H.H = I (pages: un-rotation is a second rotation)
     x = np.random.default_rng(12).standard_normal((16, 128)).astype(np.float32)
@@ -457,7 +462,8 @@ def test_key_write_fp8_bounds_and_extremes():
         # half-ulp bound of 3 mantissa bits (absolute 2^-10 in the subnormal range), in scale units
         dec = O.decode_fp8_e4m3fn(codes) * scale[:, None].astype(np.float64)
         q = x.astype(np.float64) / np.where(scale > 0, scale, 1)[:, None]
-        bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) * scale[:, None] * (1 + 1e-6)
+        # plus the float32 roundings of the multiplier, the scale and the product
+        bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) * scale[:, None] + 1e-6 * np.abs(x)
         assert np.all(np.abs(dec - x) <= bound)
 
 
