@@ -208,10 +208,11 @@ def key_write_row(dsa, inputs, torch, steps):
     ms = sum(ev[k].elapsed_ms(ev[k + 1]) for k in range(steps)) / steps
     per_row = 128 * 2 + 128 + 4
     by = S * n * per_row
-    return {"workload": "index_key_write_8x131072_bf16_to_fp8_rotated", "kernel": "key_write_kernel",
+    name = "index_key_write_8x131072_bf16_to_fp8_rotated"
+    return {"workload": name, "kernel": "key_write_kernel",
             "ms": round(ms, 5), "rows_per_s": S * n / (ms * 1e-3), "bytes_per_row": per_row,
             "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": by / (ms * 1e-3) / PEAK_HBM}}
+                         "unit": "GB/s", "frac": by / (ms * 1e-3) / PEAK_HBM, "traffic": measured_traffic(name, "key_write_kernel")}}
 
 
 # ---------------------------------------------------------------------- main
