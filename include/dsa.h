@@ -27,7 +27,7 @@
  *              and the prefill gather commits: attention over the gathered
  *              selected latent rows, values taken from the same rows.
  *  - [QKC]     same log, "GLM-DSA: allow for quantized indexer cache", and the
- *              ik_llama.cpp deepseek41 quantized-K-cache PR: cached rows are
+ *              unsloth llama.cpp PR #293 (deepseek41 quantized K cache): rows are
  *              rotated in F32 before they are stored in the cache type.
  *
  * Conventions for every entry point

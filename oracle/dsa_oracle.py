@@ -32,7 +32,7 @@ and notation of the pages:
   * the indexer-key cache write: new keys rotated in float32 and stored in the
     cache type (f16, bf16, or fp8 e4m3fn with a per-row scale) at their cache
     rows (PR #2058 "decode-correct indexer-K cache" commit; quantized indexer
-    and K caches in the ik_llama_opt log and the deepseek41 PR).  This part
+    and K caches in the ik_llama_opt log and unsloth llama.cpp PR #293).  This part
     alone runs in float32, because its stored codes are integers that a
     float decides (see its section).
 
@@ -411,9 +411,9 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
 # ik_llama.cpp PR #2058, "decode-correct indexer-K cache" commit: the batch's
 # Walsh-Hadamard-rotated indexer keys are written into the per-layer key cache
 # at kv_head, and later read back whole for scoring; ik_llama_opt log,
-# "GLM-DSA: allow for quantized indexer cache"; ik_llama.cpp PR "deepseek41
-# quantized K cache": rows are rotated in F32 and then stored in the cache
-# type.  The cache types here are f16, bf16 and fp8 e4m3fn with one f32 scale
+# "GLM-DSA: allow for quantized indexer cache"; unsloth llama.cpp PR #293
+# (deepseek41 quantized K cache): rows are rotated in F32 and then stored in
+# the cache type.  The cache types here are f16, bf16 and fp8 e4m3fn with one f32 scale
 # per row (the long-decode workload's format; not on the pages).
 #
 # Because a stored code is an integer decided by floating point, this part

@@ -3,10 +3,10 @@
 // ik_llama.cpp PR #2058, "decode-correct indexer-K cache" commit: the batch's
 // Walsh-Hadamard-rotated indexer keys are written into the key cache at the
 // batch's cache rows (kv_head), then read back whole for scoring.  The
-// ik_llama_opt log ("GLM-DSA: allow for quantized indexer cache") and the
-// deepseek41 quantized-K-cache PR store rows in a quantized cache type after
-// rotating them in F32.  Here the cache is f16, bf16, or fp8 e4m3fn with one
-// f32 scale per row.
+// ik_llama_opt log ("GLM-DSA: allow for quantized indexer cache") and unsloth
+// llama.cpp PR #293 (deepseek41 quantized K cache) store rows in a quantized
+// cache type after rotating them in F32.  Here the cache is f16, bf16, or fp8
+// e4m3fn with one f32 scale per row.
 //
 // Arithmetic (fixed bit for bit, so that every stored byte is reproducible):
 //   x  = the row in f32 (exact for f32 / bf16 / f16 inputs)
