@@ -26,6 +26,10 @@
  *  - [GATHER]  same log, openPangu port, "Gather OpenPangu DSA decode reads"
  *              and the prefill gather commits: attention over the gathered
  *              selected latent rows, values taken from the same rows.
+ *  - [HDR]     offgrid-sys llama.cpp llama-memory-hybrid-idx.h: pooled keys
+ *              persist in the index cache across batches; each micro-batch
+ *              re-pools only its new pools; an edit stales the pools from
+ *              its position on.
  *  - [QKC]     same log, "GLM-DSA: allow for quantized indexer cache", and the
  *              unsloth llama.cpp PR #293 (deepseek41 quantized K cache): rows are
  *              rotated in F32 before they are stored in the cache type.
@@ -157,6 +161,23 @@ int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx,
 int dsa_block_pool(const void* k_raw, int32_t dtype /* F32 | BF16 | F16 */,
                    int32_t S, int64_t n_kv, int32_t D, int32_t c,
                    float* pooled /* [S, n_kv / c, D] */, void* stream);
+
+/* ------------------------------------------------------------------------
+ * S1, incremental: re-pool only new or stale blocks      [HDR], [QSA]
+ *
+ * The pooled keys persist across calls in the caller's buffer; a micro-batch
+ * only appends pools, and a sequence edit stales every pool from some
+ * position on ([HDR]: pooled keys persist in the index cache across batches,
+ * the pools to re-pool per micro-batch, the stale position of an edit).  For
+ * each sequence s this recomputes exactly the blocks
+ *   from_block[s] <= b < floor(min(kv_len[s], n_kv) / c)
+ * of pooled [S, n_kv / c, D] (kv_len NULL: n_kv) and writes nothing else.
+ * A block's value does not depend on the call that pools it, so pooling in
+ * several calls equals dsa_block_pool bit for bit.  from_block [S] and
+ * kv_len [S] are device int32; from_block < 0 counts as 0.
+ * ---------------------------------------------------------------------- */
+int dsa_block_pool_update(const void* k_raw, int32_t dtype, int32_t S, int64_t n_kv, int32_t D, int32_t c,
+                          const int32_t* from_block, const int32_t* kv_len, float* pooled, void* stream);
 
 /* ------------------------------------------------------------------------
  * Indexer-key cache write: rotate new keys, store them in the cache type

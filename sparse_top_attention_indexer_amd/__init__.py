@@ -76,6 +76,7 @@ SYMBOLS = {
     "dsa_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(TopkDesc)]),
     "dsa_topk": (ctypes.c_int, [_vp, ctypes.POINTER(TopkDesc), _vp, _vp, ctypes.c_size_t, _vp]),
     "dsa_block_pool": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "dsa_block_pool_update": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "dsa_index_key_write": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _i64, _vp]),
     "dsa_sparse_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc), ctypes.c_int]),
     "dsa_sparse_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -188,6 +189,19 @@ def block_pool(k_raw, c: int, out=None):
         out = torch.empty((S, n_kv // c, D), device=k_raw.device, dtype=torch.float32)
     _check(lib().dsa_block_pool(_ptr(k_raw.contiguous()), _dt(k_raw), S, n_kv, D, c, _ptr(out), _stream()))
     return out
+
+
+def block_pool_update(k_raw, c: int, pooled, from_block, *, kv_len=None):
+    """Re-pools, in place, the blocks from_block[s] <= b < min(kv_len[s], n_kv) // c
+    of each sequence's persistent pooled keys [S, n_kv // c, D] f32
+    (dsa_block_pool_update); every other block is left as it is."""
+    _need_gpu(k_raw, pooled, from_block, kv_len)
+    S, n_kv, D = k_raw.shape
+    if not pooled.is_contiguous() or tuple(pooled.shape) != (S, n_kv // c, D) or pooled.dtype != torch.float32:
+        raise DsaError("pooled must be a contiguous [S, n_kv // c, D] float32 tensor")
+    _check(lib().dsa_block_pool_update(_ptr(k_raw.contiguous()), _dt(k_raw), S, n_kv, D, c, _ptr(_i32c(from_block)),
+                                       _ptr(_i32c(kv_len)), _ptr(pooled), _stream()))
+    return pooled
 
 
 # ------------------------------------------------------ indexer-key cache --

@@ -226,7 +226,19 @@ int dsa_block_pool(const void* k_raw, int32_t dtype, int32_t S, int64_t n_kv, in
   if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_F16) return DSA_ERR_DTYPE;
   if (S < 1 || n_kv < 1 || D < 1 || D > 4096) return DSA_ERR_SHAPE;
   if (c < 1) return DSA_ERR_PARAM;
-  return hip_status(launch_block_pool(k_raw, dtype, S, n_kv, D, c, pooled, as_stream(stream)));
+  if (!aligned16(k_raw) || !aligned16(pooled)) return DSA_ERR_ALIGN;
+  return hip_status(launch_block_pool(k_raw, dtype, S, n_kv, D, c, nullptr, nullptr, pooled, as_stream(stream)));
+}
+
+int dsa_block_pool_update(const void* k_raw, int32_t dtype, int32_t S, int64_t n_kv, int32_t D, int32_t c,
+                          const int32_t* from_block, const int32_t* kv_len, float* pooled, void* stream) {
+  if (!k_raw || !pooled || !from_block) return DSA_ERR_NULL;
+  if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_F16) return DSA_ERR_DTYPE;
+  if (S < 1 || n_kv < 1 || D < 1 || D > 4096) return DSA_ERR_SHAPE;
+  if (c < 1) return DSA_ERR_PARAM;
+  if (S * (n_kv / c) > 0x7fffffffLL) return DSA_ERR_SHAPE;
+  if (!aligned16(k_raw) || !aligned16(pooled)) return DSA_ERR_ALIGN;
+  return hip_status(launch_block_pool(k_raw, dtype, S, n_kv, D, c, from_block, kv_len, pooled, as_stream(stream)));
 }
 
 int dsa_index_key_write(const void* k_new, int32_t k_dtype, int32_t S, int64_t n_new, int32_t D,
@@ -429,7 +441,7 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
     sp.k_out = f.k_out;
     if (d->c > 1) {
       float* pooled = reinterpret_cast<float*>(ws + f.off_pooled);
-      DSA_TRY(launch_block_pool(d->k_idx, d->k_idx_dtype, d->S, d->n_kv, d->D, d->c, pooled, s));
+      DSA_TRY(launch_block_pool(d->k_idx, d->k_idx_dtype, d->S, d->n_kv, d->D, d->c, nullptr, nullptr, pooled, s));
       sp.k = pooled;
     }
     TopkParams tp = topk_params(scores, &f.topk_desc, idx);

@@ -78,7 +78,7 @@ hipError_t launch_key_write(const void* k_new, int k_dtype, int S, int64_t n_new
                             int hadamard, void* cache, int cache_dtype, float* cache_scale, int64_t n_cache,
                             hipStream_t st);
 hipError_t launch_block_pool(const void* k_raw, int dtype, int S, int64_t n_kv, int D, int c,
-                             float* pooled, hipStream_t st);
+                             const int32_t* from_block, const int32_t* kv_len, float* pooled, hipStream_t st);
 
 // --------------------------------------------------------------- attention --
 // floats per split partial record of one (row, split, head): the Dv

@@ -217,3 +217,10 @@ def indexer_queries(S: int, n_q: int, H: int = 64, seed: int = 2007) -> dict:
     q = torch.randn((S, n_q, H, 128), generator=g).to(torch.bfloat16)
     w = torch.randn((S, n_q, H), generator=g) / math.sqrt(H)
     return {"q_idx": q, "w": w}
+
+
+def raw_key_batch(S: int, n_kv: int, D: int = 128, dtype=torch.bfloat16, seed: int = 3000) -> torch.Tensor:
+    """Raw (unpooled) indexer keys [S, n_kv, D] ~ N(0,1) in dtype, as the
+    block-pooled workload stores them."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn((S, n_kv, D), generator=g).to(dtype)

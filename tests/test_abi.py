@@ -200,3 +200,16 @@ def test_index_key_write_rejects():
     assert call(had=2) == PARAM
     assert call(k=ctypes.c_void_p(FAKE + 8)) == ALIGN and call(dst=ctypes.c_void_p(FAKE + 4)) == ALIGN
     assert call(n=0) == OK and call(k=None, n=0) == OK   # nothing to write: no launch
+
+
+@no_gpu
+def test_block_pool_update_rejects():
+    L = dsa.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert L.dsa_block_pool_update(f, 1, 1, 100, 128, 4, None, None, f, None) == NULL   # from_block is required
+    assert L.dsa_block_pool_update(None, 1, 1, 100, 128, 4, f, None, f, None) == NULL
+    assert L.dsa_block_pool_update(f, 3, 1, 100, 128, 4, f, None, f, None) == DTYPE
+    assert L.dsa_block_pool_update(f, 1, 0, 100, 128, 4, f, None, f, None) == SHAPE
+    assert L.dsa_block_pool_update(f, 1, 1, 100, 128, 0, f, None, f, None) == PARAM
+    assert L.dsa_block_pool_update(ctypes.c_void_p(FAKE + 2), 1, 1, 100, 128, 4, f, None, f, None) == ALIGN
+    assert L.dsa_block_pool(f, 1, 1, 100, 128, 4, ctypes.c_void_p(FAKE + 4), None) == ALIGN
