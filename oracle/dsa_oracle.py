@@ -517,3 +517,53 @@ def index_key_write(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool):
     scale = (m * unit).astype(np.float32)
     q = (y * inv[..., None]).astype(np.float32)
     return encode_fp8_e4m3fn(q), scale
+
+
+# --------------------------------------------------------------------------
+# IndexShare: layers that reuse an earlier layer's selection.
+# --------------------------------------------------------------------------
+#
+# ik_llama_opt log, "GLM-5.2 DSA: IndexShare" commit: a layer is "full" (it
+# runs its own indexer and top-k) when il <= 1 or il % 4 == 2; every other
+# layer is "shared" and attends over the selection of the most recent full
+# layer.  The page reports that the rule gives 21 full and 57 shared layers
+# for the 78-layer model.
+
+
+def index_share_full(layer: int) -> bool:
+    """True when layer `layer` computes its own top-k."""
+    if layer < 0:
+        raise ValueError("layer index must be >= 0")
+    return layer <= 1 or layer % 4 == 2
+
+
+def index_share_source(layer: int) -> int:
+    """The layer whose selection layer `layer` attends over: itself when it is
+    full, else the most recent full layer before it."""
+    src = layer
+    while not index_share_full(src):
+        src -= 1
+    return src
+
+
+def forward_layers(layers, top_k: int, c: int, q_pos, kv_len=None, n_sink: int = 0,
+                   rotate_q: bool = False, rows: Optional[Sequence] = None):
+    """A stack of DSA attention layers under IndexShare.
+
+    layers[il] is a dict with the layer's Q, K, V, q_idx, k_idx, w (and
+    optional k_scale, scale).  Full layers run forward(); shared layers run
+    sparse_attention() over the index rows of their source layer.  Returns
+    the per-layer outputs and index rows.
+    """
+    outs, idxs = [], []
+    for il, L in enumerate(layers):
+        src = index_share_source(il)
+        if src == il:
+            O, idx, _ = forward(L["Q"], L["K"], L["V"], L["q_idx"], L["k_idx"], L["w"], top_k, c, q_pos,
+                                kv_len, L.get("k_scale"), n_sink, L.get("scale"), rotate_q, rows)
+        else:
+            idx = idxs[src]
+            O = sparse_attention(L["Q"], L["K"], L["V"], idx, q_pos, kv_len, c, L.get("scale"), rows)
+        outs.append(O)
+        idxs.append(idx)
+    return outs, idxs

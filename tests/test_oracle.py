@@ -480,3 +480,40 @@ def test_key_write_16bit_rows_and_rotation_invariance():
     assert np.abs(d_rot - q @ k.T.astype(np.float64)).max() < 2e-2
     bb, _ = O.index_key_write(k, "bf16", False)
     assert np.abs(O.decode_bf16(bb) - k).max() <= 2.0 ** -8 * np.abs(k).max()
+
+
+# ------------------------------------------------------------------ IndexShare --
+
+def test_index_share_rule_reproduces_the_page_counts():
+    # the IndexShare commit: the rule gives 21 full and 57 shared layers for the 78-layer model
+    full = [il for il in range(78) if O.index_share_full(il)]
+    assert len(full) == 21 and 78 - len(full) == 57
+    assert full[:4] == [0, 1, 2, 6] and full[-1] == 74
+
+
+def test_index_share_source_is_the_latest_full_layer():
+    for il in range(78):
+        src = O.index_share_source(il)
+        assert O.index_share_full(src) and src <= il
+        assert all(not O.index_share_full(j) for j in range(src + 1, il + 1))
+    assert [O.index_share_source(il) for il in range(8)] == [0, 1, 2, 2, 2, 2, 6, 6]
+
+
+def test_forward_layers_shares_selections():
+    # shared layers attend over their source layer's rows: a stack whose layers
+    # share one indexer input still gives each layer its own attention output
+    g = np.random.default_rng(21)
+    n, H, D, Hq, Dk = 40, 2, 128, 2, 16
+    q_pos = np.arange(n)[None, :]
+    layers = []
+    for il in range(4):
+        layers.append({"Q": g.standard_normal((1, n, Hq, Dk)), "K": g.standard_normal((1, n, Hq, Dk)),
+                       "V": g.standard_normal((1, n, Hq, Dk)), "q_idx": g.standard_normal((1, n, H, D)),
+                       "k_idx": g.standard_normal((1, n, D)), "w": g.random((1, n, H))})
+    outs, idxs = O.forward_layers(layers, 8, 1, q_pos)
+    assert np.array_equal(idxs[3], idxs[2])          # layer 3 is shared, its source is layer 2
+    assert not np.array_equal(idxs[1], idxs[0])       # full layers select on their own
+    want3 = O.sparse_attention(layers[3]["Q"], layers[3]["K"], layers[3]["V"], idxs[2], q_pos)
+    assert np.array_equal(outs[3], want3)
+    own3 = O.forward(*(layers[3][k] for k in ("Q", "K", "V", "q_idx", "k_idx", "w")), 8, 1, q_pos)[1]
+    assert not np.array_equal(own3, idxs[3])          # ... which differs from what it would select itself
