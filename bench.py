@@ -10,8 +10,9 @@ attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
                     [--no-cpu-baseline] [--no-next-rows] [--calib-copy]
 
 Beside the hot path it times the indexer-key cache write (rotate + fp8
-quantise) at the long-decode cache shape and the incremental block pooling of
-one micro-batch, reported under "next_rows".
+quantise) at the long-decode cache shape, the incremental block pooling of
+one micro-batch, and an 8-layer IndexShare decode stack, reported under
+"next_rows".
 """
 
 import argparse
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: DSA prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the rows measured beside the hot path (key-cache write, incremental pooling)")
+                    help="skip the rows measured beside the hot path (key-cache write, incremental pooling, IndexShare)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (counter calibration)")
@@ -256,6 +257,52 @@ def pool_update_row(dsa, inputs, torch, steps):
                     "blocks takes the same), not HBM"}
 
 
+# ---------------------------------------------------- next row: IndexShare
+
+def index_share_row(dsa, inputs, torch, steps):
+    """An 8-layer stack at the batched-decode shape (32 sequences x 32768
+    cached keys, 128-head MLA) under IndexShare (layers 0, 1, 2, 6 select,
+    3-5 and 7 reuse the latest full layer's rows), against the same stack with
+    every layer selecting on its own.  The layers share one set of inputs
+    (the work per layer does not depend on the values); calls are queued
+    behind a spin kernel so that the events time the GPU."""
+    wl = inputs.preset(3)
+    x = inputs.generate(wl, device="cuda")
+    layer = {k: x[k] for k in ("Q", "K", "V", "q_idx", "k_idx", "w", "k_scale")}
+    layer["scale"] = wl.scale
+    n_layers = 8
+    layers = [layer] * n_layers
+    outs = [torch.empty((wl.S, wl.n_q, wl.Hq, wl.Dv), device="cuda") for _ in range(n_layers)]
+    kw = dict(n_sink=wl.n_sink, hadamard_q=wl.hadamard_q, kv_len=x["kv_len"])
+
+    def shared():
+        dsa.forward_layers(layers, wl.top_k, wl.c, x["q_pos"], outs=outs, **kw)
+
+    def own():
+        for il in range(n_layers):
+            dsa.forward(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k, wl.c, x["q_pos"],
+                        k_scale=x["k_scale"], scale=wl.scale, out=outs[il], **kw)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [dsa.Event() for _ in range(2)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_ms(ev[1]) / steps
+
+    ms_shared, ms_own = timed(shared), timed(own)
+    full = sum(1 for il in range(n_layers) if dsa.index_share_source(il) == il)
+    return {"workload": "index_share_8_layers_batched_decode_32x32768", "layers": n_layers, "full_layers": full,
+            "ms_per_stack": round(ms_shared, 5), "ms_per_stack_all_full": round(ms_own, 5),
+            "query_tokens_per_s": wl.S * wl.n_q / (ms_shared * 1e-3), "speedup": round(ms_own / ms_shared, 3)}
+
+
 # ---------------------------------------------------------------------- main
 
 def main():
@@ -349,7 +396,8 @@ def main():
     }
     if not args.no_next_rows:
         line["next_rows"] = {"index_key_write": key_write_row(dsa, inputs, torch, 20),
-                             "block_pool_update": pool_update_row(dsa, inputs, torch, 20)}
+                             "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
+                             "index_share": index_share_row(dsa, inputs, torch, 5)}
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

@@ -30,6 +30,9 @@
  *              persist in the index cache across batches; each micro-batch
  *              re-pools only its new pools; an edit stales the pools from
  *              its position on.
+ *  - [ISHARE]  same log, "GLM-5.2 DSA: IndexShare": full layers (layer <= 1
+ *              or layer % 4 == 2) compute their own top-k, shared layers
+ *              reuse the most recent full layer's selection.
  *  - [QKC]     same log, "GLM-DSA: allow for quantized indexer cache", and the
  *              unsloth llama.cpp PR #293 (deepseek41 quantized K cache): rows are
  *              rotated in F32 before they are stored in the cache type.
@@ -213,6 +216,17 @@ int dsa_block_pool_update(const void* k_raw, int32_t dtype, int32_t S, int64_t n
 int dsa_index_key_write(const void* k_new, int32_t k_dtype, int32_t S, int64_t n_new, int32_t D,
                         const int32_t* dst_row, int32_t hadamard, void* cache, int32_t cache_dtype,
                         float* cache_scale, int64_t n_cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * IndexShare: which layer's selection a layer attends over     [ISHARE]
+ *
+ * A layer is full (it runs its own indexer and top-k: dsa_forward with
+ * idx_out) when layer <= 1 or layer % 4 == 2; every other layer is shared and
+ * attends over the index rows of the most recent full layer
+ * (dsa_sparse_attn with those rows).  Returns that layer (the layer itself
+ * when it is full), or DSA_ERR_PARAM for layer < 0.  Host-only; no launch.
+ * ---------------------------------------------------------------------- */
+int32_t dsa_index_share_source(int32_t layer);
 
 /* ------------------------------------------------------------------------
  * S4 + S5 (+ S6): sparse attention over the selected tokens   [GATHER], [PR2058]

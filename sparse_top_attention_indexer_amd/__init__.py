@@ -77,6 +77,7 @@ SYMBOLS = {
     "dsa_topk": (ctypes.c_int, [_vp, ctypes.POINTER(TopkDesc), _vp, _vp, ctypes.c_size_t, _vp]),
     "dsa_block_pool": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
     "dsa_block_pool_update": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "dsa_index_share_source": (ctypes.c_int32, [ctypes.c_int32]),
     "dsa_index_key_write": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _i64, _vp]),
     "dsa_sparse_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnDesc), ctypes.c_int]),
     "dsa_sparse_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -351,3 +352,37 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, compress_ratio: int, q_pos, *,
     if return_scores:
         res.append(scores_out)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# --------------------------------------------------------------- IndexShare --
+
+def index_share_source(layer: int) -> int:
+    """The layer whose selection `layer` attends over (dsa_index_share_source)."""
+    r = lib().dsa_index_share_source(layer)
+    if r < 0:
+        _check(r)
+    return r
+
+
+def forward_layers(layers, top_k: int, compress_ratio: int, q_pos, *, n_sink: int = 0, hadamard_q: bool = False,
+                   kv_len=None, outs=None):
+    """A stack of DSA attention layers under IndexShare: full layers run
+    dsa_forward and keep their index rows, shared layers run dsa_sparse_attn
+    over the rows of their source layer.  layers[il] is a dict with Q, K, V,
+    q_idx, k_idx, w (optional k_scale, scale).  Returns (outputs, index rows)."""
+    res, idxs = [], []
+    for il, L in enumerate(layers):
+        src = index_share_source(il)
+        out = None if outs is None else outs[il]
+        if src == il:
+            O, idx = forward(L["Q"], L["K"], L["V"], L["q_idx"], L["k_idx"], L["w"], top_k, compress_ratio, q_pos,
+                             k_scale=L.get("k_scale"), n_sink=n_sink, scale=L.get("scale"), hadamard_q=hadamard_q,
+                             kv_len=kv_len, out=out, return_idx=True)
+        else:
+            idx = idxs[src]
+            O = sparse_attn(L["Q"], L["K"], L["V"], q_pos, idx, c=compress_ratio, kv_len=kv_len,
+                            scale=L.get("scale"), out=out)
+        res.append(O)
+        idxs.append(idx)
+    return res, idxs
+

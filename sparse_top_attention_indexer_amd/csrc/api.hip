@@ -241,6 +241,13 @@ int dsa_block_pool_update(const void* k_raw, int32_t dtype, int32_t S, int64_t n
   return hip_status(launch_block_pool(k_raw, dtype, S, n_kv, D, c, from_block, kv_len, pooled, as_stream(stream)));
 }
 
+int32_t dsa_index_share_source(int32_t layer) {
+  if (layer < 0) return DSA_ERR_PARAM;
+  auto full = [](int32_t il) { return il <= 1 || il % 4 == 2; };
+  while (!full(layer)) --layer;
+  return layer;
+}
+
 int dsa_index_key_write(const void* k_new, int32_t k_dtype, int32_t S, int64_t n_new, int32_t D,
                         const int32_t* dst_row, int32_t hadamard, void* cache, int32_t cache_dtype,
                         float* cache_scale, int64_t n_cache, void* stream) {

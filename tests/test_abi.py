@@ -213,3 +213,11 @@ def test_block_pool_update_rejects():
     assert L.dsa_block_pool_update(f, 1, 1, 100, 128, 0, f, None, f, None) == PARAM
     assert L.dsa_block_pool_update(ctypes.c_void_p(FAKE + 2), 1, 1, 100, 128, 4, f, None, f, None) == ALIGN
     assert L.dsa_block_pool(f, 1, 1, 100, 128, 4, ctypes.c_void_p(FAKE + 4), None) == ALIGN
+
+
+def test_index_share_rule_matches_the_oracle():
+    # host-only export: the layer rule, no launch
+    from oracle import dsa_oracle as O
+    L = dsa.lib()
+    assert L.dsa_index_share_source(-1) == PARAM
+    assert [L.dsa_index_share_source(il) for il in range(200)] == [O.index_share_source(il) for il in range(200)]
