@@ -7,7 +7,7 @@ line.  The default workload is the 4096-token DSA prefill (128-head MLA
 attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1..5]
-                    [--no-cpu-baseline] [--no-next-rows] [--calib-copy]
+                    [--no-cpu-baseline] [--no-next-rows] [--no-flush] [--calib-copy]
 
 Beside the hot path it times the indexer-key cache write (rotate + fp8
 quantise) at the long-decode cache shape, the incremental block pooling of
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: DSA prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not evict the caches before each timed step (warm-cache timing by wall clock)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the rows measured beside the hot path (key-cache write, incremental pooling, IndexShare)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
@@ -330,15 +332,24 @@ def main():
         dsa.forward(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k, wl.c, x["q_pos"],
                     out=out, workspace=ws, phase_events=events, **kw)
 
+    # Before each timed step a 1 GiB read evicts the L2s and the 256 MB
+    # Infinity Cache, so that a step finds its inputs in HBM, as it would
+    # after the other layers of a model ran.  A read leaves clean lines (a
+    # write would leave dirty ones for the step to write back).  The flush
+    # runs before the step's first library event, never inside the step.
+    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if flush is not None:
+            flush.amax()
         step(ev[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
+    step_ms = sorted(ev[k][0].elapsed_ms(ev[k][4]) for k in range(args.steps))
+    ms_step = sum(step_ms) / args.steps if flush is not None else elapsed * 1e3 / args.steps
 
     # per-phase times from the HIP events recorded on the library's stream
     names = ["scores", "topk", "attn", "combine"]
@@ -390,6 +401,12 @@ def main():
                    "top_k": wl.top_k, "compress_ratio": wl.c, "n_sink": wl.n_sink, "attention": wl.attn,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "dk": wl.Dk, "dv": wl.Dv,
                    "scored_pairs": pairs_score, "attended_pairs": pairs_attn},
+        "timing": {"cache": "flushed before each step (1 GiB read)" if flush is not None else "warm",
+                   "step_ms_median": round(step_ms[len(step_ms) // 2], 5),
+                   "step_ms_p10": round(step_ms[int(0.1 * (len(step_ms) - 1))], 5),
+                   "step_ms_p90": round(step_ms[int(0.9 * (len(step_ms) - 1))], 5),
+                   "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+                   "step_clock": "HIP events around each step" if flush is not None else "wall clock"},
         "phases_ms": {k_: round(v_, 5) for k_, v_ in phase_ms.items()},
         "phase_roofline_frac": {k_: round(v_["frac"], 4) for k_, v_ in per_phase.items()},
         "roofline": roof,
