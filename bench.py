@@ -7,7 +7,8 @@ line.  The default workload is the 4096-token DSA prefill (128-head MLA
 attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1..5]
-                    [--no-cpu-baseline] [--no-next-rows] [--no-flush] [--calib-copy]
+                    [--no-cpu-baseline] [--no-next-rows] [--next-rows-only] [--no-flush]
+                    [--calib-copy]
 
 Beside the hot path it times the indexer-key cache write (rotate + fp8
 quantise) at the long-decode cache shape, the incremental block pooling of
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not evict the caches before each timed step (warm-cache timing by wall clock)")
+    ap.add_argument("--next-rows-only", action="store_true",
+                    help="only the rows measured beside the hot path, as one JSON object (for kernel traces)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the rows measured beside the hot path (key-cache write, incremental pooling, IndexShare)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
@@ -317,6 +320,11 @@ def main():
     import sparse_top_attention_indexer_amd as dsa
     from sparse_top_attention_indexer_amd import inputs
 
+    if args.next_rows_only:
+        print(json.dumps({"next_rows": {"index_key_write": key_write_row(dsa, inputs, torch, 20),
+                                        "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
+                                        "index_share": index_share_row(dsa, inputs, torch, 5)}}), flush=True)
+        return
     wl = inputs.preset(args.config)
     dev = "cuda"
     x = inputs.generate(wl, device=dev)
