@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 // Prefill variant (n_q a multiple of 4, no histogram): one workgroup = 4
 // consecutive query rows of one sequence (one wave each) x one chunk of
 // 32-key tiles.  The key tiles are gathered once per workgroup into LDS with
-// direct global -> LDS loads, two tiles ahead (three tile buffers), and read
-// by all four waves.  Three workgroups share a CU (148 registers, 40 KB of
+// direct global -> LDS loads, three tiles ahead (four tile buffers), and read
+// by all four waves.  Three workgroups share a CU (148 registers, 48 KB of
 // LDS), so that three waves per SIMD interleave their products and
 // epilogues; with a rotated or non-bf16 q split into two operands, two
 // workgroups (more registers).  The scores of the chunk
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 // c ^ (r & 15), so that a wave's B-operand read (lane n: row n, chunk
 // 8 h2 + ks) is free of LDS bank conflicts.
 constexpr int SC_TILE_BYTES = 32 * 256;   // one key tile
-constexpr int SC_NBUF = 3;                      // tiles: computing, landed, in flight
+constexpr int SC_NBUF = 4;                      // tiles: computing, landed, two in flight
 constexpr int SC_MAX_TILES = 32;                // chunk_tiles bound for this kernel
 constexpr size_t SC_LDS = SC_NBUF * SC_TILE_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
 
@@ -395,6 +395,7 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   };
   if (n_t > 0) issue(0);
   if (n_t > 1) issue(1);
+  if (n_t > 2) issue(2);
 
   u32x4_t qa[RB][8][NQ];
   float wv[RB][16];
@@ -431,11 +432,12 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   };
 
   for (int T = 0; T < n_t; ++T) {
-    // tile T has landed: only the two loads of tile T + 1 may still be in flight
-    if (T + 1 < n_t) __builtin_amdgcn_s_waitcnt(0x0f72);   // vmcnt(2)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
-    __syncthreads();                                        // for every wave; slot of T - 1 free
-    if (T + 2 < n_t) issue(T + 2);
+    // tile T has landed: only the loads of tiles T + 1 and T + 2 (two each) may still be in flight
+    if (T + 2 < n_t) __builtin_amdgcn_s_waitcnt(0x0f74);        // vmcnt(4)
+    else if (T + 1 < n_t) __builtin_amdgcn_s_waitcnt(0x0f72);   // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
+    __syncthreads();                                             // for every wave; slot of T - 1 free
+    if (T + 3 < n_t) issue(T + 3);
     if (T < t_own) {
       const uint8_t* kt = s_kt + (T % SC_NBUF) * SC_TILE_BYTES + b_off;
       uint32_t hx = 8u * h2;
