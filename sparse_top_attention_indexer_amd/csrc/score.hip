@@ -443,7 +443,9 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
       uint32_t hx = 8u * h2;
       asm volatile("" : "+v"(hx));
       f32x16_t acc0[RB];
+      __builtin_amdgcn_s_setprio(1);   // the product chain first; the other waves' epilogues fill the gaps
       products(kt, hx, acc0);
+      __builtin_amdgcn_s_setprio(0);
       epilogue(acc0, T);
     }
   }
