@@ -56,8 +56,7 @@ struct TopkParams {
   uint32_t* cand_cnt;    // [rows]
   uint32_t* cand;        // [rows][cand_cap][2] (key, index)
   uint32_t* cnt_hi;      // [rows][n_chunks]
-  uint32_t* offs;        // [rows][n_chunks]
-  uint32_t* thr;         // [rows][4]: b1, T, J, flags
+  uint32_t* thr;         // [rows][4]: b1, -, -, units above b1
   int64_t cand_cap;
   int32_t chunk;         // units per multi-block chunk
   int32_t n_chunks;

@@ -17,8 +17,8 @@
 //   - long rows with few of them (decode): many workgroups per row.  A global
 //     histogram of the top 12 bits (built by the score epilogue in the fused
 //     path) locates the threshold bin; units of that bin are gathered as
-//     candidates; one workgroup per row resolves the exact threshold among
-//     the candidates; the row is then compacted chunk by chunk.
+//     candidates; then every chunk's workgroup resolves the exact threshold
+//     among the row's candidates itself and compacts its chunk.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -271,109 +271,85 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   }
 }
 
-// Exact threshold among the candidates of one row, per-chunk output offsets,
-// the forced sinks and the -1 padding.
-__global__ __launch_bounds__(256) void topk_resolve_kernel(TopkParams p) {
-  __shared__ uint32_t s_hist[HIST_BINS];
-  __shared__ uint32_t s_scr[16];
-  extern __shared__ uint32_t s_chunk[];   // n_chunks selected-candidate counters
-  const int64_t row = blockIdx.x;
-  const RowInfo ri = row_info(p, row);
-  int32_t* out = p.idx + row * p.k_out;
+// Exact threshold key T among the candidates of one row, and the largest
+// kept index J among the candidates equal to T (0xffffffff when every one of
+// them is kept).  The candidates are the units of the threshold bin b1 (the
+// units above it are kept whole); radix passes of 12 + 8 bits on the low 20
+// bits of the key find T, then, only when the tie at T is cut, 11 + 11 + 10
+// bits on the complemented index find J (the need-th smallest index).  The
+// candidate order does not matter, so the result is deterministic.  All 256
+// threads call it; need > 0.
+__device__ void resolve_threshold(const TopkParams& p, int64_t row, uint32_t need, uint32_t* s_hist,
+                                  uint32_t* s_scr, uint32_t* T_out, uint32_t* J_out) {
   const int tid = threadIdx.x;
-  if (ri.n_vis <= p.k_out) {
-    for (int64_t j = tid; j < p.k_out; j += 256) out[j] = j < ri.n_vis ? static_cast<int32_t>(j) : -1;
-    return;
-  }
-  for (int64_t j = tid; j < p.k_out; j += 256) {
-    if (j < ri.nf) out[j] = static_cast<int32_t>(j);
-    else if (j >= ri.K) out[j] = -1;
-  }
-  uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
-  uint32_t T = 0xffffffffu, J = 0;
-  bool none = need == 0;
   const uint32_t* cand = p.cand + row * p.cand_cap * 2;
-  const uint32_t m = none ? 0 : p.cand_cnt[row];
-  if (!none) {
-    need -= p.thr[row * 4 + 3];            // minus the units above the threshold bin
-    const uint32_t b1 = p.thr[row * 4 + 0];
-    // low 20 bits of the key: 12 + 8
-    uint32_t prefix = b1 << 20, pmask = 0xfff00000u;
-    const int shifts[2] = {8, 0};
-    const int nbits[2] = {12, 8};
-    uint32_t n_eq = 0;   // candidates whose key equals T
-    for (int pass = 0; pass < 2; ++pass) {
-      const int nb = 1 << nbits[pass], sh = shifts[pass];
-      for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
-      __syncthreads();
-      for (uint32_t e = tid; e < m; e += 256) {
-        const uint32_t k = cand[2 * e];
-        if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      uint32_t above;
-      const uint32_t b = find_bin_desc(s_hist, nb, need, s_scr, &above);
-      need -= above;
-      prefix |= b << sh;
-      pmask |= static_cast<uint32_t>(nb - 1) << sh;
-      if (pass == 1) n_eq = s_hist[b];   // read before the next pass clears the bins
-    }
-    T = prefix;
+  const uint32_t m = p.cand_cnt[row];
+  need -= p.thr[row * 4 + 3];            // minus the units above the threshold bin
+  const uint32_t b1 = p.thr[row * 4 + 0];
+  uint32_t prefix = b1 << 20, pmask = 0xfff00000u;
+  const int shifts[2] = {8, 0};
+  const int nbits[2] = {12, 8};
+  uint32_t n_eq = 0;   // candidates whose key equals T
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nb = 1 << nbits[pass], sh = shifts[pass];
+    for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
     __syncthreads();
-    // the need-th smallest index among candidates equal to T: radix select on
-    // the complemented index (largest complement = smallest index), 3 x 11 bits;
-    // when every candidate equal to T is kept (no tie is cut, the usual
-    // case), the largest index does
-    const bool cut = n_eq > need;
-    uint32_t jp = 0, jm = 0;
-    const int jsh[3] = {21, 10, 0};
-    const int jbits[3] = {11, 11, 10};
-    for (int pass = 0; pass < (cut ? 3 : 0); ++pass) {
-      const int nb = 1 << jbits[pass], sh = jsh[pass];
-      for (int b = tid; b < HIST_BINS; b += 256) s_hist[b] = 0;
-      __syncthreads();
-      for (uint32_t e = tid; e < m; e += 256) {
-        if (cand[2 * e] != T) continue;
-        const uint32_t cj = ~cand[2 * e + 1];
-        if ((cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      uint32_t above;
-      const uint32_t b = find_bin_desc(s_hist, nb < 256 ? 256 : nb, need, s_scr, &above);
-      need -= above;
-      jp |= b << sh;
-      jm |= static_cast<uint32_t>(nb - 1) << sh;
+    for (uint32_t e = tid; e < m; e += 256) {
+      const uint32_t k = cand[2 * e];
+      if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
     }
-    J = cut ? ~jp : 0xffffffffu;
+    __syncthreads();
+    uint32_t above;
+    const uint32_t b = find_bin_desc(s_hist, nb, need, s_scr, &above);
+    need -= above;
+    prefix |= b << sh;
+    pmask |= static_cast<uint32_t>(nb - 1) << sh;
+    if (pass == 1) n_eq = s_hist[b];   // read before the next pass clears the bins
   }
-  // per-chunk counts of selected candidates, then output offsets
-  for (int c = tid; c < p.n_chunks; c += 256) s_chunk[c] = 0;
+  const uint32_t T = prefix;
   __syncthreads();
-  for (uint32_t e = tid; e < m; e += 256) {
-    const uint32_t k = cand[2 * e], j = cand[2 * e + 1];
-    if (k > T || (k == T && j <= J)) atomicAdd(&s_chunk[j / p.chunk], 1u);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t acc = static_cast<uint32_t>(ri.nf);
-    for (int c = 0; c < p.n_chunks; ++c) {
-      p.offs[row * p.n_chunks + c] = acc;
-      acc += p.cnt_hi[row * p.n_chunks + c] + s_chunk[c];
+  const bool cut = n_eq > need;
+  uint32_t jp = 0, jm = 0;
+  const int jsh[3] = {21, 10, 0};
+  const int jbits[3] = {11, 11, 10};
+  for (int pass = 0; pass < (cut ? 3 : 0); ++pass) {
+    const int nb = 1 << jbits[pass], sh = jsh[pass];
+    for (int b = tid; b < HIST_BINS; b += 256) s_hist[b] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < m; e += 256) {
+      if (cand[2 * e] != T) continue;
+      const uint32_t cj = ~cand[2 * e + 1];
+      if ((cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
     }
-    p.thr[row * 4 + 1] = T;
-    p.thr[row * 4 + 2] = J;
+    __syncthreads();
+    uint32_t above;
+    const uint32_t b = find_bin_desc(s_hist, nb < 256 ? 256 : nb, need, s_scr, &above);
+    need -= above;
+    jp |= b << sh;
+    jm |= static_cast<uint32_t>(nb - 1) << sh;
   }
+  *T_out = T;
+  *J_out = cut ? ~jp : 0xffffffffu;
 }
 
-// Ordered compaction of one chunk of a row: thread t owns the 16 units
-// 16 t .. 16 t + 15 of the chunk (loaded first, as four 16-byte loads), so an
-// exclusive scan of the per-thread counts gives ascending output positions.
-__global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
+// Resolve and ordered compaction of one chunk of a row.  Every workgroup of a
+// row resolves (T, J) from the row's candidates on its own (the candidates of
+// one 12-bit bin: a few thousand at most, read from L2), so no single
+// workgroup per row stands between the select and the compaction.  The
+// chunk's output offset is the forced sinks plus the units kept in earlier
+// chunks: those above the threshold bin (counted by the select) and the kept
+// candidates.  Thread t then owns the 16 units 16 t .. 16 t + 15 of the chunk
+// (loaded first, as four 16-byte loads), so an exclusive scan of the
+// per-thread counts gives ascending output positions.  Chunk 0 also writes the
+// sinks and the -1 padding, or the whole row when every visible unit is kept.
+__global__ __launch_bounds__(256) void topk_finish_kernel(TopkParams p) {
+  __shared__ uint32_t s_hist[HIST_BINS];
   __shared__ uint32_t s_scr[16];
   const int64_t row = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x % p.n_chunks;
+  const int tid = threadIdx.x;
   const int64_t c0 = static_cast<int64_t>(ch) * TOPK_CHUNK;
-  const int64_t a0 = c0 + 16 * threadIdx.x;
+  const int64_t a0 = c0 + 16 * tid;
   const float* sc = p.scores + row * p.n_units;
   float v[16];
   if (a0 + 16 <= p.n_units && (p.n_units & 3) == 0) {   // whole, 16-byte aligned run
@@ -389,10 +365,36 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = a0 + i < p.n_units ? sc[a0 + i] : 0.f;
   }
-  const uint32_t T = p.thr[row * 4 + 1], J = p.thr[row * 4 + 2];
-  const uint32_t off = p.offs[row * p.n_chunks + ch];
   const RowInfo ri = row_info(p, row);
-  if (ri.n_vis <= p.k_out || ri.K == ri.nf) return;
+  int32_t* out = p.idx + row * p.k_out;
+  if (ri.n_vis <= p.k_out) {
+    if (ch == 0)
+      for (int64_t j = tid; j < p.k_out; j += 256) out[j] = j < ri.n_vis ? static_cast<int32_t>(j) : -1;
+    return;
+  }
+  if (ch == 0) {
+    for (int64_t j = tid; j < p.k_out; j += 256) {
+      if (j < ri.nf) out[j] = static_cast<int32_t>(j);
+      else if (j >= ri.K) out[j] = -1;
+    }
+  }
+  if (ri.K == ri.nf) return;
+  uint32_t T, J;
+  resolve_threshold(p, row, static_cast<uint32_t>(ri.K - ri.nf), s_hist, s_scr, &T, &J);
+  // units kept before this chunk
+  uint32_t before = 0;
+  for (int c = tid; c < ch; c += 256) before += p.cnt_hi[row * p.n_chunks + c];
+  {
+    const uint32_t* cand = p.cand + row * p.cand_cap * 2;
+    const uint32_t m = p.cand_cnt[row];
+    for (uint32_t e = tid; e < m; e += 256) {
+      const uint32_t k = cand[2 * e], j = cand[2 * e + 1];
+      before += j < c0 && (k > T || (k == T && j <= J));
+    }
+  }
+  uint32_t tot_before;
+  block_excl_scan_256(before, s_scr, &tot_before);
+  const uint32_t off = static_cast<uint32_t>(ri.nf) + tot_before;
   const int64_t j0 = c0 > ri.nf ? c0 : ri.nf;
   const int64_t j1 = c0 + TOPK_CHUNK < ri.n_vis ? c0 + TOPK_CHUNK : ri.n_vis;
   uint32_t sel = 0;   // bit i: unit a0 + i is kept
@@ -405,7 +407,6 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
   }
   uint32_t tot;
   uint32_t pos = off + block_excl_scan_256(__builtin_popcount(sel), s_scr, &tot);
-  int32_t* out = p.idx + row * p.k_out;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if ((sel >> i) & 1u) {
@@ -430,7 +431,7 @@ size_t topk_workspace_bytes(int64_t rows, int64_t n_units) {
   b += align256(rows * HIST_BINS * 4);
   b += align256(rows * 4);
   b += align256(rows * n_units * 8);
-  b += align256(rows * nch * 4) * 2;
+  b += align256(rows * nch * 4);
   b += align256(rows * 16);
   return b;
 }
@@ -445,7 +446,6 @@ void topk_bind_workspace(TopkParams& p, void* ws) {
   p.cand_cnt = reinterpret_cast<uint32_t*>(c); c += align256(rows * 4);
   p.cand = reinterpret_cast<uint32_t*>(c);     c += align256(rows * p.n_units * 8);
   p.cnt_hi = reinterpret_cast<uint32_t*>(c);   c += align256(rows * p.n_chunks * 4);
-  p.offs = reinterpret_cast<uint32_t*>(c);     c += align256(rows * p.n_chunks * 4);
   p.thr = reinterpret_cast<uint32_t*>(c);
 }
 
@@ -478,10 +478,7 @@ hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
   }
   hipLaunchKernelGGL(topk_select_kernel, g, dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<unsigned>(rows)), dim3(256),
-                     p.n_chunks * sizeof(uint32_t), st, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_compact_kernel, g, dim3(256), 0, st, p);
+  hipLaunchKernelGGL(topk_finish_kernel, g, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
