@@ -588,10 +588,19 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
 constexpr int GQA_D = 128;
 constexpr int GQA_VT = TILE * GQA_D * 2;   // one V tile of one wave in LDS (8 KB)
 
-// LDS of a GQA workgroup: two V tiles per wave, the stream scratch, and the
+// LDS of a GQA workgroup (one wave): two V tiles, the stream scratch, and the
 // row's block list in block mode
 static size_t gqa_lds_bytes(const AttnParams& p) {
-  return 4 * 2 * GQA_VT + 64 + (p.idx != nullptr && p.c > 1 ? static_cast<size_t>(p.k_sel) * 4 : 0);
+  return 2 * GQA_VT + 64 + (p.idx != nullptr && p.c > 1 ? static_cast<size_t>(p.k_sel) * 4 : 0);
+}
+
+// Workgroups of the GQA kernel: one per (query row, stream chunk, KV group).
+// Workgroup b runs on XCD b % 8; when the group count divides 8, the group is
+// taken from b % 8, so that each XCD's L2 holds the K/V rows of one group
+// (of an XCD pair, for 4 groups) instead of all of them.
+static int64_t gqa_grid(const AttnParams& p) {
+  const int64_t n = static_cast<int64_t>(p.S) * p.n_q * p.n_split * p.Hkv;
+  return 8 % p.Hkv == 0 ? (n + 7) / 8 * 8 : n;
 }
 
 struct GqaK {   // K fragments of one tile: key block mb, contraction step ks
@@ -601,10 +610,10 @@ struct GqaV {   // one lane's share of a V tile: rows 4 i + lane / 16, 16-byte c
   u32x4_t v[8];
 };
 
-// One workgroup = one query row x one stream chunk x 4 KV groups; wave w owns
-// KV group g = 4 * blockIdx.y + w and its G <= 16 query heads (the MFMA
-// columns, padded to 16).  After the stream set-up every wave runs its own
-// pipeline over tiles of 32 stream entries, with no workgroup barrier: the
+// One workgroup = one wave = one query row x one stream chunk x one KV group
+// g and its G <= 16 query heads (the MFMA columns, padded to 16); see
+// gqa_grid for the group of a workgroup.  After the stream set-up the wave
+// runs its own pipeline over tiles of 32 stream entries: the
 // token ids of tile j + 3 are fetched while tile j is computed; the K
 // fragments of tile j + 1 (A operand of S^T = K Q^T, straight from the cache
 // rows) and its V rows (coalesced, 1 KB per load) are in flight in registers;
@@ -615,25 +624,33 @@ struct GqaV {   // one lane's share of a V tile: rows 4 i + lane / 16, 16-byte c
 // conflicts.  With 8 heads per KV group the gathered K/V rows (16 KB per tile
 // and group) outweigh the products: the kernel is bound by L2 / last-level
 // cache bandwidth, not by the MFMAs.
-__global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnParams p) {
+__global__ __launch_bounds__(64, 2) void attn_gqa_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t s_raw[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* s_vt = s_raw + wid * (2 * GQA_VT);
-  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_raw + 4 * 2 * GQA_VT);
+  const int lane = threadIdx.x;
+  uint8_t* s_vt = s_raw;
+  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_raw + 2 * GQA_VT);
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);
 
-  const int64_t row = blockIdx.x / p.n_split;
-  const int sp = blockIdx.x % p.n_split;
+  const int64_t b = blockIdx.x;
+  int64_t unit;   // (row, chunk)
+  int g;
+  if (8 % p.Hkv == 0) {
+    g = static_cast<int>((b & 7) % p.Hkv);
+    unit = (b >> 3) * (8 / p.Hkv) + (b & 7) / p.Hkv;
+  } else {
+    g = static_cast<int>(b % p.Hkv);
+    unit = b / p.Hkv;
+  }
+  if (unit >= static_cast<int64_t>(p.S) * p.n_q * p.n_split) return;   // padding of the last group of 8
+  const int64_t row = unit / p.n_split;
+  const int sp = static_cast<int>(unit % p.n_split);
   const int s = static_cast<int>(row / p.n_q);
-  const StreamInfo si = stream_setup<4>(p, row, s_blk, s_scr);   // the last workgroup barrier
+  const StreamInfo si = stream_setup<1>(p, row, s_blk, s_scr);
   int64_t p0, p1;
   split_range(p, sp, si.len, &p0, &p1);
   const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
 
   const int G = p.Hq / p.Hkv;
-  const int g = blockIdx.y * 4 + wid;
-  if (g >= p.Hkv) return;
   const int col = lane & 15, quad = lane >> 4;
   const bool hvalid = col < G;
   const int head = g * G + col;
@@ -1028,8 +1045,8 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
       if (e != hipSuccess) return e;
       attr = true;
     }
-    hipLaunchKernelGGL(attn_gqa_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hkv + 3) / 4),
-                       dim3(256), gqa_lds_bytes(p), st, p);
+    hipLaunchKernelGGL(attn_gqa_kernel, dim3(static_cast<unsigned>(gqa_grid(p))), dim3(64), gqa_lds_bytes(p), st,
+                       p);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(static_cast<unsigned>(rows * p.Hq * p.n_split)), dim3(64),
                        F32_LDS, st, p);
