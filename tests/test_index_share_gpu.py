@@ -21,8 +21,9 @@ pytestmark = pytest.mark.gpu
 f64 = O.to_f64
 
 
-def test_layer_stack_shares_selections():
-    wl = inputs.mini(3)
+@pytest.mark.parametrize("n", [3, 4])   # 3: token mode, MLA decode; 4: block mode (QSA), GQA prefill chunk
+def test_layer_stack_shares_selections(n):
+    wl = inputs.mini(n)
     n_layers = 7
     xs = [inputs.generate(wl, seed=4000 + il) for il in range(n_layers)]
     ds = [dev(x) for x in xs]
@@ -35,28 +36,31 @@ def test_layer_stack_shares_selections():
     assert srcs == [O.index_share_source(il) for il in range(n_layers)] == [0, 1, 2, 2, 2, 2, 6]
 
     qp, kv = xs[0]["q_pos"].numpy(), xs[0]["kv_len"].numpy()
+    rows = [(s, i) for s in range(wl.S) for i in range(0, wl.n_q, max(1, wl.n_q // 6))]   # a spread of rows
     ol = [dict({k: (None if x[k] is None else f64(x[k])) for k in keys}, scale=wl.scale) for x in xs]
-    ref_outs, ref_idxs = O.forward_layers(ol, wl.top_k, wl.c, qp, kv, wl.n_sink, wl.hadamard_q)
-    rows = [(s, 0) for s in range(wl.S)]
+    ref_outs, ref_idxs = O.forward_layers(ol, wl.top_k, wl.c, qp, kv, wl.n_sink if wl.c == 1 else 0,
+                                          wl.hadamard_q, rows)
     worst_own, worst_ref = 0.0, 0.0
     for il in range(n_layers):
         got_idx = idxs[il].cpu().numpy().astype(np.int64)
         if srcs[il] != il:
             assert idxs[il] is idxs[srcs[il]]   # the source layer's rows, not a selection of its own
         else:
-            s_ref = oracle_scores(xs[il], wl)
+            pooled = O.block_pool(f64(xs[il]["k_idx"]), wl.c) if wl.c > 1 else None
+            s_ref = oracle_scores(xs[il], wl, rows=rows, pooled=pooled)
             for s, i in rows:
-                n_vis = O.visible_tokens(int(qp[s, i]), int(kv[s]))
-                check_selection(got_idx[s, i], ref_idxs[il][s, i], s_ref[s, i], n_vis, wl.k_out, wl.n_sink)
+                n_units = O.visible_tokens(int(qp[s, i]), int(kv[s])) // wl.c
+                check_selection(got_idx[s, i], ref_idxs[il][s, i], s_ref[s, i], n_units, wl.k_out,
+                                wl.n_sink if wl.c == 1 else 0)
         # the layer's attention over the rows it was given, against the oracle on the same rows
-        want = O.sparse_attention(ol[il]["Q"], ol[il]["K"], ol[il]["V"], got_idx, qp, kv, wl.c, wl.scale)
+        want = O.sparse_attention(ol[il]["Q"], ol[il]["K"], ol[il]["V"], got_idx, qp, kv, wl.c, wl.scale, rows)
         got = outs[il].cpu().double().numpy()
-        worst_own = max(worst_own, float(np.abs(got - want).max()))
+        worst_own = max(worst_own, max(float(np.abs(got[s, i] - want[s, i]).max()) for s, i in rows))
         # and end to end where the selections agree
         same = [(s, i) for s, i in rows if np.array_equal(got_idx[s, i], ref_idxs[il][s, i])]
         for s, i in same:
             worst_ref = max(worst_ref, float(np.abs(got[s, i] - ref_outs[il][s, i]).max()))
-    print(f"index share, {n_layers} layers: |O - oracle(same rows)| {worst_own:.2e}, "
+    print(f"index share, {wl.name}, {n_layers} layers: |O - oracle(same rows)| {worst_own:.2e}, "
           f"|O - oracle stack| {worst_ref:.2e}")
     assert worst_own <= 2e-2 and worst_ref <= 2e-2
 
