@@ -529,3 +529,39 @@ class _LazySeq:
 
 def arr(t):
     return f64(t) if isinstance(t, torch.Tensor) else t
+
+
+def test_gqa_block_mode_list_order_repeats_and_dead_rows():
+    # block mode with blocks of 64 and 8 heads per KV group: two sequences (one
+    # with fewer stored keys), 44 rows, one row that sees nothing, and a second
+    # index list with every row's blocks shuffled, one block listed twice (it
+    # is attended once per listing) and -1 entries mixed in.
+    wl = replace(inputs.mini(4), name="qsa_tiles", S=2, n_q=44, n_kv=3000, q_pos0=2956, c=64, top_k=640)
+    x = inputs.generate(wl)
+    x["kv_len"] = torch.tensor([3000, 2600], dtype=torch.int32)
+    x["q_pos"][1, 5] = -1
+    d = dev(x)
+    qp, kv = x["q_pos"].numpy(), x["kv_len"].numpy()
+    ref_idx, _ = _oracle_idx(x, wl)
+    rng = np.random.default_rng(7)
+    mixed = ref_idx.copy()
+    for s in range(wl.S):
+        for i in range(wl.n_q):
+            row = mixed[s, i]
+            live = row[row >= 0]
+            if live.size >= 2:
+                perm = rng.permutation(live)
+                perm[-1] = perm[0]   # one block listed twice (the last distinct one dropped)
+                row[:] = -1
+                start = 1 if live.size < row.size else 0   # a -1 in front where the row has room
+                row[start:start + live.size] = perm
+    rows = [(s, i) for s in range(wl.S) for i in range(wl.n_q)]
+    worst = 0.0
+    for idx in (ref_idx, mixed):
+        got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], torch.from_numpy(idx.astype(np.int32)).to(DEV),
+                              c=wl.c, kv_len=d["kv_len"], scale=wl.scale).cpu().double().numpy()
+        ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), idx, qp, kv, wl.c, wl.scale)
+        worst = max(worst, float(np.abs(got - ref).max()))
+        assert np.all(got[1, 5] == 0.0)
+    print(f"gqa block mode, shuffled and repeated lists: max |O - oracle| {worst:.2e}")
+    assert worst <= 2e-2
