@@ -183,7 +183,13 @@ def cpu_baseline(wl, x, budget_s):
         done += 1
         if t_total > budget_s and done >= 4:
             break
-    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads, "cpu_model": model, "kind": "oracle",
             "sample": f"{done} of {len(rows)} query rows of the {wl.name} batch, taken in bit-reversed order "
                       f"(evenly spread), numpy float64 oracle, {t_total:.1f} s"}
 
@@ -358,6 +364,16 @@ def main():
     elapsed = time.perf_counter() - t0
     step_ms = sorted(ev[k][0].elapsed_ms(ev[k][4]) for k in range(args.steps))
     ms_step = sum(step_ms) / args.steps if flush is not None else elapsed * 1e3 / args.steps
+    warm_ms = None
+    if flush is not None:   # the same steps back to back with warm caches, labelled as such
+        n_warm = max(1, min(args.steps, 10))
+        ew = [dsa.Event() for _ in range(2)]
+        ew[0].record()
+        for _ in range(n_warm):
+            step()
+        ew[1].record()
+        torch.cuda.synchronize()
+        warm_ms = ew[0].elapsed_ms(ew[1]) / n_warm
 
     # per-phase times from the HIP events recorded on the library's stream
     names = ["scores", "topk", "attn", "combine"]
@@ -414,6 +430,7 @@ def main():
                    "step_ms_p10": round(step_ms[int(0.1 * (len(step_ms) - 1))], 5),
                    "step_ms_p90": round(step_ms[int(0.9 * (len(step_ms) - 1))], 5),
                    "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+                   "warm_cache_ms_per_step": None if warm_ms is None else round(warm_ms, 5),
                    "step_clock": "HIP events around each step" if flush is not None else "wall clock"},
         "phases_ms": {k_: round(v_, 5) for k_, v_ in phase_ms.items()},
         "phase_roofline_frac": {k_: round(v_["frac"], 4) for k_, v_ in per_phase.items()},

@@ -495,7 +495,12 @@ def test_forward_matches_oracle_full_size_sampled(n):
     checked on sampled rows."""
     wl = inputs.preset(n)
     d = inputs.generate(wl, device=DEV)
-    rows = _rows_sample(wl, 16 if wl.n_q > 1 else wl.S, seed=10 + n)
+    rows = _rows_sample(wl, 20 if wl.n_q > 1 else wl.S, seed=10 + n)
+    # and the rows at the dense threshold: visible length top_k (+ c - 1 in block mode) -1 .. +2
+    qp_all = d["q_pos"].cpu().numpy()
+    thr = wl.top_k + (wl.c - 1 if wl.c > 1 else 0)
+    edge = [(s, i) for s in range(wl.S) for i in range(wl.n_q) if thr - 1 <= qp_all[s, i] + 1 <= thr + 2]
+    rows = sorted(set(rows) | set(edge[:8]))
     # the oracle gets CPU copies of what the sampled rows read; the attention
     # rows move to the host only when the oracle indexes them
     x = {"q_pos": d["q_pos"].cpu(), "kv_len": d["kv_len"].cpu(), "w": d["w"].cpu(), "q_idx": d["q_idx"].cpu(),
