@@ -170,7 +170,8 @@ def cpu_baseline(wl, x, budget_s):
     K = [f(x["K"][s:s + 1]) for s in range(wl.S)]
     V = [f(x["V"][s:s + 1]) for s in range(wl.S)]
     kv = x["kv_len"].cpu().numpy()
-    done, t_total = 0, 0.0
+    done, t_total, scored = 0, 0.0, 0
+    kvn = x["kv_len"].cpu().numpy()
     for s, i in sample:
         qi = f(x["q_idx"][s:s + 1, i:i + 1])
         w = f(x["w"][s:s + 1, i:i + 1])
@@ -181,6 +182,8 @@ def cpu_baseline(wl, x, budget_s):
                   wl.n_sink if wl.c == 1 else 0, wl.scale, wl.hadamard_q)
         t_total += time.perf_counter() - t0
         done += 1
+        n_vis = max(0, min(int(qp[0, 0]) + 1, int(kvn[s]), wl.n_kv))
+        scored += n_vis // wl.c
         if t_total > budget_s and done >= 4:
             break
     model = "unknown"
@@ -189,7 +192,8 @@ def cpu_baseline(wl, x, budget_s):
             model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads, "cpu_model": model, "kind": "oracle",
+    return {"value": done / t_total, "unit": "query tokens/s", "keys_scored_per_s": scored / t_total,
+            "cores": threads, "cpu_model": model, "kind": "oracle",
             "sample": f"{done} of {len(rows)} query rows of the {wl.name} batch, taken in bit-reversed order "
                       f"(evenly spread), numpy float64 oracle, {t_total:.1f} s"}
 
