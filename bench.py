@@ -451,6 +451,11 @@ def main():
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        if args.config in (1, 3):   # the small and the batched-decode workloads also on one core
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(wl, x, args.cpu_seconds / 2)
+            line["cpu_baseline"]["one_core"] = {k: one[k] for k in ("value", "keys_scored_per_s", "sample")}
     print(json.dumps(line), flush=True)
 
 
