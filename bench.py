@@ -323,8 +323,8 @@ def index_share_row(dsa, inputs, torch, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs on one GPU "
+              "and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
     import sparse_top_attention_indexer_amd as dsa

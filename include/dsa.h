@@ -82,7 +82,7 @@ typedef enum {
 #define DSA_ERR_ALIGN (-5)       /* pointer or row stride not 16-byte aligned */
 #define DSA_ERR_WORKSPACE (-6)   /* workspace NULL or smaller than required  */
 #define DSA_ERR_HIP (-7)         /* the HIP runtime reported a launch error  */
-#define DSA_ERR_UNSUPPORTED (-8) /* a valid shape this build has no kernel for */
+#define DSA_ERR_UNSUPPORTED (-8) /* a valid shape the library has no kernel for */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dsa_strerror(int status);

@@ -423,7 +423,7 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
 # 16-bit caches, a multiplication by float32(1/sqrt(128)); every step is one
 # correctly rounded float32 operation, so the result is fixed bit for bit.
 #
-# fp8 rows (this build's format; the pages fix only that rows are rotated in
+# fp8 rows (the library's own format; the pages fix only that rows are rotated in
 # F32 before they are stored in the cache type): with y the row after the butterflies (not yet
 # normalised) and m = max |y|, code = e4m3fn(y * (448 / m)) and scale =
 # m * float32(1 / (448 sqrt(128))) (1 / 448 for an unrotated row), so that
