@@ -216,38 +216,47 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   const bool wvalid = head0 < p.Hq;   // Hq is a multiple of 16
   const int head = head0 + col;
 
-  // Contraction step ks takes four 8-dim chunks, one per lane group q: for
-  // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
-  // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
-  // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
-  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk; loaded
-  // first, so that they are in flight during the stream set-up.
-  u32x4_t qf[18];
-  {
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
+  // In token mode the stream is the idx row itself (its length k_sel needs no
+  // load), so the row's first 2 TOK_RING entries are fetched first: the token
+  // ring and the gather of the first two tiles wait for them, while the Q
+  // fragments are only needed by the first score products.
+  const bool token_mode = p.idx != nullptr && p.c == 1;
+  constexpr int RPT0 = TOK_RING / (64 * NW);   // ring entries per thread
+  static_assert(RPT0 * 64 * NW == TOK_RING, "the ring is filled in whole passes");
+  int64_t p0 = 0, p1 = 0;
+  int32_t pre[2 * RPT0];
+  if (token_mode) {
+    split_range(p, sp, p.k_sel, &p0, &p1);
+    const int32_t* ir = p.idx + row * p.k_sel;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
-      qf[ks] = wvalid ? *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 2 * RPT0; ++j) {
+      const int64_t e = p0 + tid + 64 * NW * j;
+      pre[j] = e < p1 ? ir[e] : -1;
     }
   }
 
   const StreamInfo si = stream_setup<NW>(p, row, s_blk, s_scr);
-  int64_t p0, p1;
-  split_range(p, sp, si.len, &p0, &p1);
+  if (!token_mode) split_range(p, sp, si.len, &p0, &p1);
   // The token ring takes the first TOK_RING stream entries.  In token mode
   // the trailing dead entries (the -1 padding of short selections) are cut
   // off in the same pass over the index row; they would add nothing.
   uint32_t last = 0;   // 1 + offset of the last live entry
-  for (int i = tid; i < TOK_RING; i += 64 * NW) {
-    const int32_t t = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
+#pragma unroll
+  for (int j = 0; j < RPT0; ++j) {
+    const int i = tid + 64 * NW * j;
+    int32_t t;
+    if (token_mode) t = pre[j] >= 0 && pre[j] < si.n_vis ? pre[j] : -1;
+    else t = p0 + i < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, p0 + i)) : -1;
     s_tok[i] = t;
     if (t >= 0) last = static_cast<uint32_t>(i + 1);
   }
-  const bool trim = p.idx != nullptr && p.c == 1 && p1 > p0;
+  const bool trim = token_mode && p1 > p0;
   if (trim) {
+#pragma unroll
+    for (int j = RPT0; j < 2 * RPT0; ++j)
+      if (pre[j] >= 0 && pre[j] < si.n_vis) last = static_cast<uint32_t>(tid + 64 * NW * j + 1);
     const int32_t* ir = p.idx + row * p.k_sel;
-    for (int64_t e = p0 + TOK_RING + tid; e < p1; e += 64 * NW) {
+    for (int64_t e = p0 + 2 * TOK_RING + tid; e < p1; e += 64 * NW) {
       const int32_t v = ir[e];
       if (v >= 0 && v < si.n_vis) last = static_cast<uint32_t>(e - p0 + 1);
     }
@@ -255,6 +264,26 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     for (int o = 32; o >= 1; o >>= 1) last = max(last, static_cast<uint32_t>(__shfl_xor(static_cast<int>(last), o, 64)));
     if (lane == 0) s_scr[8 + wid] = last;
   }
+  // Contraction step ks takes four 8-dim chunks, one per lane group q: for
+  // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
+  // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
+  // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
+  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk.  Issued
+  // once the ring is filled (vector loads complete in issue order, so the
+  // ring's index loads would otherwise queue behind these 147 KB per row);
+  // they land while the first two tiles are gathered.  A wave without heads
+  // (Hq < 128) loads head 0's query in every column; its outputs are never
+  // written.
+  u32x4_t qf[18];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
+      qf[ks] = *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk);
+    }
+  }
+
   __syncthreads();   // the ring and the per-wave ends
   if (trim) {
     uint32_t e = 0;
@@ -470,7 +499,6 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   // segment 32 j + 1, land by the wait that closes segment 32 j + 2, and are
   // validated and stored in segment 32 j + 3, into the slots of tiles
   // 16 j - 16 .. 16 j - 1, which segment 32 j read last
-  const bool token_mode = p.idx != nullptr && p.c == 1;
   constexpr int RPT = 16 * TILE / (64 * NW);   // refill entries per thread
   int32_t ring_v[RPT];
 #pragma unroll
@@ -503,11 +531,32 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     if ((sg & 1) == (grp == 0 ? 1 : 0)) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this group's loads have landed
     __syncthreads();
   };
+  // accumulator (db, j) holds dim 16 db + 4 q + j of head `head`
+  auto write_out = [&]() __attribute__((always_inline)) {
+    if (!(wvalid && head < p.Hq)) return;
+    if (p.n_split == 1) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * q;
+#pragma unroll
+      for (int db = 0; db < 32; ++db)
+        store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+    } else {
+      float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(MLA_DV);
+#pragma unroll
+      for (int db = 0; db < 32; ++db)
+        *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
+      if (q == 0) {
+        pp[MLA_DV] = m_run;
+        pp[MLA_DV + 1] = l_run;
+      }
+    }
+  };
+
   // Segment sg: waves 0..3 compute the scores and softmax of tile sg / 2
   // (even sg) or its PV products (odd sg); waves 4..7 do the same one segment
   // later.  Waves without
-  // heads (Hq < 128) run the same products on zero queries, so that every wave
-  // takes the same straight-line path.
+  // heads (Hq < 128) run the same products on head 0's query, so that
+  // every wave takes the same straight-line path.
   using plan_hi = std::integral_constant<int, 1>;   // the gather share of waves 4..7
   using plan_lo = std::integral_constant<int, 2>;   // the gather share of waves 0..3
   if (grp == 0) {
@@ -533,7 +582,10 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       }
       segment_end(2 * u + 1);
     }
+    // the last segment is the other group's last PV: this group's outputs
+    // are final and are written meanwhile
     segment_io(2 * n_tiles);
+    write_out();
     segment_end(2 * n_tiles);
   } else {
     segment_io(0);
@@ -562,25 +614,7 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       segment_end(2 * u + 2);
     }
   }
-  if (!(wvalid && head < p.Hq)) return;
-
-  // accumulator (db, j) holds dim 16 db + 4 q + j of head `head`
-  if (p.n_split == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * q;
-#pragma unroll
-    for (int db = 0; db < 32; ++db)
-      store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
-  } else {
-    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(MLA_DV);
-#pragma unroll
-    for (int db = 0; db < 32; ++db)
-      *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
-    if (q == 0) {
-      pp[MLA_DV] = m_run;
-      pp[MLA_DV + 1] = l_run;
-    }
-  }
+  if (grp == 1) write_out();
 }
 
 // ============================================================== GQA kernel ==
