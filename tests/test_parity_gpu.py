@@ -327,6 +327,32 @@ def test_mla_head_counts_and_block_mode(case):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("case", ["mla_48_heads_split", "mla_144_heads"])
+def test_mla_writes_only_its_output(case):
+    # Waves without heads (48 heads: waves 3..7 of every workgroup; 144: waves
+    # 1..7 of the second head block) run their products on head 0's query and
+    # must write nothing.  The output sits inside a NaN-filled buffer whose
+    # margins (as long as a whole row of 128 heads) must come back untouched;
+    # every output element must be written, with the bits of a plain call.
+    wl = MLA_SHAPE_CASES[case]()
+    x = inputs.generate(wl)
+    idx, _ = _oracle_idx(x, wl)
+    d = dev(x)
+    idx_d = torch.from_numpy(idx).to(torch.int32).to(DEV)
+    kw = dict(c=wl.c, kv_len=d["kv_len"], scale=wl.scale)
+    plain = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], idx_d, **kw)
+    n, margin = plain.numel(), 128 * 512
+    buf = torch.full((n + 2 * margin,), float("nan"), dtype=torch.float32, device=DEV)
+    out = buf[margin:margin + n].view(plain.shape)
+    dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], idx_d, out=out, **kw)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.isnan(b[:margin]).all() and torch.isnan(b[margin + n:]).all()
+    got = b[margin:margin + n]
+    assert not torch.isnan(got).any()
+    assert torch.equal(got.view(torch.int32), plain.cpu().reshape(-1).view(torch.int32))
+
+
 def test_attention_bf16_output_and_empty_rows():
     wl = inputs.mini(2)
     x = inputs.generate(wl)
