@@ -11,9 +11,11 @@
 // attention over the gathered latent rows, values taken from the same rows).
 //
 // The stream is cut into tiles of 32 entries.  An online softmax runs over the
-// tiles in order; invisible or dead entries are masked by position (their rows
-// are zero-filled and their logits -inf, never multiplied), and a row that sees
-// no key at all is written as zeros.  Long streams are split into contiguous
+// tiles in order; invisible or dead entries are masked by position: their
+// logits are -inf, so their weights are exactly zero.  The GQA and f32 kernels
+// zero-fill their rows; the MLA kernel gathers the sequence's row 0 in their
+// place (a written, visible row whenever the stream has a live entry), which
+// its zero weight cancels.  A row that sees no key at all is written as zeros.  Long streams are split into contiguous
 // chunks whose partial (max, sum, unnormalised output) are merged in a fixed
 // order by attn_combine_kernel, so results are deterministic and identical for
 // the same stream whatever the call that produced it.
