@@ -15,10 +15,11 @@
 // logits are -inf, so their weights are exactly zero.  The GQA and f32 kernels
 // zero-fill their rows; the MLA kernel gathers the sequence's row 0 in their
 // place (a written, visible row whenever the stream has a live entry), which
-// its zero weight cancels.  A row that sees no key at all is written as zeros.  Long streams are split into contiguous
-// chunks whose partial (max, sum, unnormalised output) are merged in a fixed
-// order by attn_combine_kernel, so results are deterministic and identical for
-// the same stream whatever the call that produced it.
+// its zero weight cancels.  A row that sees no key at all is written as
+// zeros.  Long streams are split into contiguous chunks whose partial (max,
+// sum, unnormalised output) are merged in a fixed order by
+// attn_combine_kernel, so results are deterministic and identical for the
+// same stream whatever the call that produced it.
 //
 // Kernels:
 //   attn_f32_kernel   f32 Q/K/V, any head grouping, Dk, Dv <= 256 (VALU)
