@@ -32,9 +32,13 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
-// Order-preserving map float -> uint32: a < b (as floats, -0 < +0) iff key(a) < key(b).
+// Order-preserving map float -> uint32: a < b as floats iff key(a) < key(b).
+// -0 and +0 compare equal, so both take the key of +0: equal scores tie, and
+// a tie goes to the lower index whatever the signs of the zeros (a score is
+// -0 when every head's ReLU is zero and the head weights are negative).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
+  u = u == 0x80000000u ? 0u : u;
   return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 

@@ -200,6 +200,15 @@ def test_topk_ties_go_to_lowest_index():
     assert O.topk_row(sc, 7, 4).tolist() == [1, 2, 3, 4]
 
 
+def test_topk_signed_zeros_are_equal_scores():
+    # IEEE -0 == +0: zeros of either sign tie, and the tie goes to the lowest
+    # index (a +0 after a -0 is not ranked above it)
+    sc = np.array([-0.0, 0.0, -0.0, 0.0, 1.0, -0.0, -1.0])
+    assert O.topk_row(sc, 7, 3).tolist() == [0, 1, 4]
+    assert O.topk_row(sc, 7, 4).tolist() == [0, 1, 2, 4]
+    assert O.topk_row(sc[::-1].copy(), 7, 3).tolist() == [1, 2, 3]
+
+
 def test_topk_short_rows_keep_everything_and_pad():
     sc = np.array([[[0.3, -2.0, 1.0, 7.0, -np.inf, -np.inf]]])
     idx = O.topk(sc, np.array([[3]]), 5)

@@ -177,6 +177,12 @@ def _topk_case(S, n_q, n_units, top_k, c=1, n_sink=0, kind="normal", q_pos=None,
 def test_topk_rows_in_lds_causal():
     n = 3000
     _topk_case(1, 300, n, 256, q_pos=torch.arange(n - 300, n, dtype=torch.int32)[None] - 700)
+    # rows of every length on the long-row kernel (n_units > 2048): fewer keys
+    # than top_k, then candidate counts below 512, 512..2048 and above 2048,
+    # which load their keys 1, 4 and 16 at a time per thread; plain and tied
+    q_pos = torch.arange(0, n, 47, dtype=torch.int32)[None]
+    _topk_case(1, q_pos.shape[1], n, 100, q_pos=q_pos, n_sink=1, seed=14)
+    _topk_case(1, q_pos.shape[1], n, 100, q_pos=q_pos, kind="ties", seed=15)
 
 
 def test_topk_rows_in_lds_with_ties_and_sink():
@@ -201,6 +207,22 @@ def test_topk_multiblock_decode_rows():
 def test_topk_multiblock_ties_and_equal():
     _topk_case(2, 1, 50000, 1000, kind="ties", seed=5)
     _topk_case(1, 1, 30000, 999, kind="equal", seed=6)
+
+
+@pytest.mark.parametrize("S,n_q,n,k,seed", [(1, 8, 1000, 100, 16), (1, 8, 5000, 700, 17), (2, 1, 40000, 2048, 18)])
+def test_topk_signed_zero_ties(S, n_q, n, k, seed):
+    # -0 and +0 are equal scores: they tie, and the tie goes to the lower
+    # index.  About 98 % of the scores are zeros of random sign, so every row
+    # cuts its tie at zero: the short- and long-row kernels and the
+    # multi-block decode path
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((S, n_q, n), generator=g)
+    sc = torch.where(x < 2.0, torch.zeros_like(x) * torch.sign(x), x)
+    assert bool((torch.signbit(sc) & (sc == 0)).any()) and bool((~torch.signbit(sc) & (sc == 0)).any())
+    q_pos = torch.full((S, n_q), n - 1, dtype=torch.int32)
+    got = dsa.topk(sc.to(DEV), q_pos.to(DEV), k).cpu().numpy()
+    ref = O.topk(sc.double().numpy(), q_pos.numpy(), k)
+    assert np.array_equal(got, ref)
 
 
 def test_topk_edge_rows():
