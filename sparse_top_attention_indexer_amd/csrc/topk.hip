@@ -93,6 +93,32 @@ __device__ uint32_t find_bin_desc(const uint32_t* hist, int nb, uint32_t need, u
 // run 16 t .. 16 t + 15, words 17 t + i) free of bank conflicts.
 __device__ __forceinline__ int64_t key_slot(int64_t e) { return e + (e >> 4); }
 
+// Keys e = tid, tid + 256, ... below m of a row into LDS.  Each thread issues
+// the loads of NB keys before converting any (in-range addresses only: past m
+// it reloads key m - 1), so a row of 4096 keys costs one memory latency
+// instead of sixteen; NB follows the row's length, so that short rows do not
+// issue loads they do not use.
+template <int NB>
+__device__ __forceinline__ void load_row_keys(const float* sc, int64_t m, uint32_t* s_key) {
+  for (int64_t e0 = threadIdx.x; e0 < m; e0 += 256 * NB) {
+    float v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t e = e0 + 256 * i;
+      v[i] = sc[e < m ? e : m - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t e = e0 + 256 * i;
+      if (e < m) s_key[key_slot(e)] = order_key(v[i]);
+    }
+  }
+}
+
+// LONG: rows may exceed 2048 units.  Only then are the batched key loads
+// compiled in: their registers (77 VGPRs against 36) would cost launches of
+// short rows (pooled blocks, small LDS) two of their eight waves per SIMD.
+template <bool LONG>
 __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   extern __shared__ uint32_t s_mem[];
   uint32_t* s_hist = s_mem;                 // HIST_BINS
@@ -110,7 +136,13 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   const int64_t m = ri.n_vis - ri.nf;             // candidates: units nf .. n_vis-1
   const uint32_t need0 = static_cast<uint32_t>(ri.K - ri.nf);
   const float* sc = p.scores + row * p.n_units + ri.nf;
-  for (int64_t e = tid; e < m; e += 256) s_key[key_slot(e)] = order_key(sc[e]);
+  if constexpr (LONG) {
+    if (m > 256 * 8) load_row_keys<16>(sc, m, s_key);
+    else if (m > 256 * 2) load_row_keys<4>(sc, m, s_key);
+    else load_row_keys<1>(sc, m, s_key);
+  } else {
+    load_row_keys<1>(sc, m, s_key);
+  }
   for (int64_t j = tid; j < p.k_out; j += 256) {
     if (j < ri.nf) out[j] = static_cast<int32_t>(j);
     else if (j >= ri.K) out[j] = -1;
@@ -196,7 +228,17 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
   if (j0 < ri.nf) j0 = ri.nf;
   if (j1 > ri.n_vis) j1 = ri.n_vis;
   const float* sc = p.scores + row * p.n_units;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) atomicAdd(&s_hist[order_key(sc[j]) >> 20], 1u);
+  for (int64_t jb = j0 + threadIdx.x; jb < j1; jb += 256 * 16) {   // 16 loads in flight per thread
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = jb + 256 * i;
+      v[i] = sc[j < j1 ? j : j1 - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (jb + 256 * i < j1) atomicAdd(&s_hist[order_key(v[i]) >> 20], 1u);
+  }
   __syncthreads();
   uint32_t* g = p.hist + row * HIST_BINS;
   for (int b = threadIdx.x; b < HIST_BINS; b += 256)
@@ -216,12 +258,17 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   const int ch = blockIdx.x % p.n_chunks;
   const int64_t c0 = static_cast<int64_t>(ch) * TOPK_CHUNK;
   const float* sc = p.scores + row * p.n_units;
-  uint32_t key[16];
+  // all 16 loads are issued before any key is used (in-range addresses only:
+  // past the row's end a lane reloads its last unit)
+  float v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t j = c0 + 256 * i + threadIdx.x;
-    key[i] = j < p.n_units ? order_key(sc[j]) : 0u;
+    v[i] = sc[j < p.n_units ? j : p.n_units - 1];
   }
+  uint32_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) key[i] = c0 + 256 * i + threadIdx.x < p.n_units ? order_key(v[i]) : 0u;
   const RowInfo ri = row_info(p, row);
   if (ri.n_vis <= p.k_out) return;
   const uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
@@ -271,6 +318,26 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   }
 }
 
+// Calls f(key, index) for candidates e = tid, tid + 256, ... below m (this
+// thread's share, in that order), with the loads of 8 candidates issued
+// before any is used: the candidates come from L2, and a row of a few
+// thousand then costs one latency per 2048 instead of one per 256.
+template <typename F>
+__device__ __forceinline__ void for_candidates(const uint32_t* cand, uint32_t m, F&& f) {
+  constexpr int CB = 8;
+  for (uint32_t e0 = threadIdx.x; e0 < m; e0 += 256 * CB) {
+    u32x2_t kv[CB];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const uint32_t e = e0 + 256 * i;
+      kv[i] = *reinterpret_cast<const u32x2_t*>(cand + 2 * static_cast<size_t>(e < m ? e : m - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      if (e0 + 256 * i < m) f(kv[i].x, kv[i].y);
+  }
+}
+
 // Exact threshold key T among the candidates of one row, and the largest
 // kept index J among the candidates equal to T (0xffffffff when every one of
 // them is kept).  The candidates are the units of the threshold bin b1 (the
@@ -294,10 +361,9 @@ __device__ void resolve_threshold(const TopkParams& p, int64_t row, uint32_t nee
     const int nb = 1 << nbits[pass], sh = shifts[pass];
     for (int b = tid; b < nb; b += 256) s_hist[b] = 0;
     __syncthreads();
-    for (uint32_t e = tid; e < m; e += 256) {
-      const uint32_t k = cand[2 * e];
+    for_candidates(cand, m, [&](uint32_t k, uint32_t) {
       if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
-    }
+    });
     __syncthreads();
     uint32_t above;
     const uint32_t b = find_bin_desc(s_hist, nb, need, s_scr, &above);
@@ -316,11 +382,10 @@ __device__ void resolve_threshold(const TopkParams& p, int64_t row, uint32_t nee
     const int nb = 1 << jbits[pass], sh = jsh[pass];
     for (int b = tid; b < HIST_BINS; b += 256) s_hist[b] = 0;
     __syncthreads();
-    for (uint32_t e = tid; e < m; e += 256) {
-      if (cand[2 * e] != T) continue;
-      const uint32_t cj = ~cand[2 * e + 1];
-      if ((cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
-    }
+    for_candidates(cand, m, [&](uint32_t k, uint32_t j) {
+      const uint32_t cj = ~j;
+      if (k == T && (cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
+    });
     __syncthreads();
     uint32_t above;
     const uint32_t b = find_bin_desc(s_hist, nb < 256 ? 256 : nb, need, s_scr, &above);
@@ -387,10 +452,7 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkParams p) {
   {
     const uint32_t* cand = p.cand + row * p.cand_cap * 2;
     const uint32_t m = p.cand_cnt[row];
-    for (uint32_t e = tid; e < m; e += 256) {
-      const uint32_t k = cand[2 * e], j = cand[2 * e + 1];
-      before += j < c0 && (k > T || (k == T && j <= J));
-    }
+    for_candidates(cand, m, [&](uint32_t k, uint32_t j) { before += j < c0 && (k > T || (k == T && j <= J)); });
   }
   uint32_t tot_before;
   block_excl_scan_256(before, s_scr, &tot_before);
@@ -461,12 +523,15 @@ hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   if (!topk_use_multiblock(rows, p.n_units)) {
     const size_t lds = (HIST_BINS + 16 + static_cast<size_t>(p.n_units + p.n_units / 16 + 1)) * sizeof(uint32_t);
+    const bool long_rows = p.n_units > 2048;
+    const void* fn = long_rows ? reinterpret_cast<const void*>(topk_row_kernel<true>)
+                               : reinterpret_cast<const void*>(topk_row_kernel<false>);
     if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_row_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(topk_row_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
+    if (long_rows) hipLaunchKernelGGL(topk_row_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
+    else hipLaunchKernelGGL(topk_row_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
     return hipGetLastError();
   }
   const dim3 g(static_cast<unsigned>(rows * p.n_chunks));
