@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
 // histogram, and stay in registers for both passes.
 static_assert(TOPK_CHUNK == 16 * 256, "16 keys per thread");
 __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
-  __shared__ uint32_t s_hist[HIST_BINS];
+  __shared__ __align__(16) uint32_t s_hist[HIST_BINS];
   __shared__ uint32_t s_scr[16];
   __shared__ uint32_t s_base;
   const int64_t row = blockIdx.x / p.n_chunks;
@@ -273,8 +273,14 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkParams p) {
   if (ri.n_vis <= p.k_out) return;
   const uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
   if (need == 0) return;
-  const uint32_t* g = p.hist + row * HIST_BINS;
-  for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = g[b];
+  // the row's histogram (16 KB, in L2 after the score kernel's atomics):
+  // every thread issues its four 16-byte loads before it writes any
+  const u32x4_t* g4 = reinterpret_cast<const u32x4_t*>(p.hist + row * HIST_BINS);
+  u32x4_t hv[HIST_BINS / 1024];
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / 1024; ++i) hv[i] = g4[threadIdx.x + 256 * i];
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / 1024; ++i) reinterpret_cast<u32x4_t*>(s_hist)[threadIdx.x + 256 * i] = hv[i];
   __syncthreads();
   uint32_t above;
   const uint32_t b1 = find_bin_desc(s_hist, HIST_BINS, need, s_scr, &above);
