@@ -39,7 +39,8 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers, row-major, last dimension
- *    innermost.  The caller allocates every buffer, including the workspace;
+ *    innermost.  The caller allocates every buffer, including the workspace
+ *    (16-byte aligned, like every tensor pointer, else DSA_ERR_ALIGN);
  *    the library allocates nothing, keeps no pointer after returning and holds
  *    no global state.  Calls are asynchronous on the given stream (a
  *    hipStream_t passed as void*; NULL = the default stream); buffers must stay

@@ -215,6 +215,7 @@ int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx, void* wo
   if (st) return st;
   const size_t need = dsa_topk_workspace_bytes(d);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
   TopkParams p = topk_params(scores, d, idx);
   if (need) topk_bind_workspace(p, workspace);
   return hip_status(launch_topk(p, false, as_stream(stream)));
@@ -278,6 +279,7 @@ int dsa_sparse_attn(const dsa_attn_desc* d, const int32_t* idx, void* out, void*
   AttnParams p = attn_params(d, idx, out);
   const size_t need = attn_workspace_bytes(p);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
   p.part = static_cast<float*>(workspace);
   return hip_status(launch_attention(p, as_stream(stream)));
 }
@@ -410,6 +412,7 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
   const int st = plan_forward(d, &f);
   if (st) return st;
   if (f.total && (!workspace || workspace_bytes < f.total)) return DSA_ERR_WORKSPACE;
+  if (f.total && !aligned16(workspace)) return DSA_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   void* const* ev = d->phase_events;

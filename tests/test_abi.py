@@ -101,6 +101,8 @@ def test_topk_workspace_rule():
                       None) == WORKSPACE
     assert L.dsa_topk(ctypes.c_void_p(FAKE), ctypes.byref(long), ctypes.c_void_p(FAKE),
                       ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
+    assert L.dsa_topk(ctypes.c_void_p(FAKE), ctypes.byref(long), ctypes.c_void_p(FAKE),
+                      ctypes.c_void_p(FAKE + 8), need, None) == ALIGN   # the workspace is 16-byte aligned too
 
 
 @no_gpu
@@ -147,6 +149,8 @@ def test_sparse_attn_workspace_rule():
     assert need > 0            # few rows: the stream is split and merged
     assert L.dsa_sparse_attn(ctypes.byref(decode), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
                              ctypes.c_void_p(FAKE), need - 4, None) == WORKSPACE
+    assert L.dsa_sparse_attn(ctypes.byref(decode), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE + 4), need, None) == ALIGN
     prefill = _mla(S=1, n_q=4096, n_kv=4096, k_sel=2048)
     assert L.dsa_sparse_attn_workspace_bytes(ctypes.byref(prefill), 0) == 0
 
@@ -182,6 +186,7 @@ def test_forward_workspace_covers_intermediates():
     assert need >= 4096 * 4096 * 4 + 4096 * 2048 * 4   # scores + idx
     assert L.dsa_forward(ctypes.byref(prefill), ctypes.c_void_p(FAKE), need - 1, None) == WORKSPACE
     assert L.dsa_forward(ctypes.byref(prefill), None, need, None) == WORKSPACE
+    assert L.dsa_forward(ctypes.byref(prefill), ctypes.c_void_p(FAKE + 8), need, None) == ALIGN
 
 
 @no_gpu
