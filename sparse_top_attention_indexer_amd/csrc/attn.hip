@@ -220,9 +220,10 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   const int head = head0 + col;
 
   // In token mode the stream is the idx row itself (its length k_sel needs no
-  // load), so the row's first 2 TOK_RING entries are fetched first: the token
-  // ring and the gather of the first two tiles wait for them, while the Q
-  // fragments are only needed by the first score products.
+  // load), so the row's first 2 TOK_RING entries are fetched first, then the Q
+  // fragments.  Vector loads complete in issue order: the token ring waits for
+  // the index entries alone while Q is still in flight, and Q lands while the
+  // ring is filled and the first two tiles are gathered.
   const bool token_mode = p.idx != nullptr && p.c == 1;
   constexpr int RPT0 = TOK_RING / (64 * NW);   // ring entries per thread
   static_assert(RPT0 * 64 * NW == TOK_RING, "the ring is filled in whole passes");
@@ -235,6 +236,25 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     for (int j = 0; j < 2 * RPT0; ++j) {
       const int64_t e = p0 + tid + 64 * NW * j;
       pre[j] = e < p1 ? ir[e] : -1;
+    }
+  }
+
+  // Contraction step ks takes four 8-dim chunks, one per lane group q: for
+  // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
+  // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
+  // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
+  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk (147 KB
+  // per row), issued behind the index entries.  The loads are unconditional,
+  // so that the wait before the ring counts exactly; a wave without heads
+  // (Hq < 128) loads head 0's query in every column, and its outputs are
+  // never written.
+  u32x4_t qf[18];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
+      qf[ks] = *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk);
     }
   }
 
@@ -267,26 +287,6 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     for (int o = 32; o >= 1; o >>= 1) last = max(last, static_cast<uint32_t>(__shfl_xor(static_cast<int>(last), o, 64)));
     if (lane == 0) s_scr[8 + wid] = last;
   }
-  // Contraction step ks takes four 8-dim chunks, one per lane group q: for
-  // ks < 16 chunk 16 (ks >> 2) + 4 q + (ks & 3), for ks = 16, 17 the rope chunk
-  // 64 + 2 q + ks - 16 (a fixed permutation of the 576 dims, the same for K and
-  // Q; this spread keeps the 16-byte LDS reads free of bank conflicts).
-  // Q^T fragments: lane (head col, q) holds the 8 dims of its chunk.  Issued
-  // once the ring is filled (vector loads complete in issue order, so the
-  // ring's index loads would otherwise queue behind these 147 KB per row);
-  // they land while the first two tiles are gathered.  A wave without heads
-  // (Hq < 128) loads head 0's query in every column; its outputs are never
-  // written.
-  u32x4_t qf[18];
-  {
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
-      qf[ks] = *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk);
-    }
-  }
-
   __syncthreads();   // the ring and the per-wave ends
   if (trim) {
     uint32_t e = 0;
