@@ -375,6 +375,35 @@ def test_mla_writes_only_its_output(case):
     assert torch.equal(got.view(torch.int32), plain.cpu().reshape(-1).view(torch.int32))
 
 
+def test_mla_long_token_lists_and_trimmed_tails():
+    # Token lists of 3000 entries, longer than the 2048 the MLA prologue
+    # fetches up front, on one stream per row (130 rows: no split).  The live
+    # entries end before 1024, between 1024 and 2048, or past 2048, and a dead
+    # (-1) and an invisible id sit inside every list: the trim of the trailing
+    # dead entries past the prefetched window, and the token ring refills.
+    wl = inputs.Workload("mla_long_list", 1, 130, 4000, 3870, 32, 128, torch.bfloat16, torch.bfloat16, "normal",
+                         0.2, 2048, 1, 0, False, "mla", 128, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=97)
+    x = inputs.generate(wl)
+    k_sel, ends = 3000, [700, 1500, 2600, 3000]
+    g = np.random.default_rng(97)
+    qp = x["q_pos"].numpy()
+    idx = np.full((1, wl.n_q, k_sel), -1, dtype=np.int32)
+    for i in range(wl.n_q):
+        n_vis, live = int(qp[0, i]) + 1, ends[i % 4]
+        idx[0, i, :live] = g.permutation(n_vis)[:live]
+        idx[0, i, 3] = -1
+        idx[0, i, 7] = n_vis + 5 if n_vis + 5 < wl.n_kv else -1   # a key after the query
+    d = dev(x)
+    got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], torch.from_numpy(idx).to(DEV), kv_len=d["kv_len"],
+                          scale=wl.scale).cpu().double().numpy()
+    rows = [(0, i) for i in (0, 1, 2, 3, 64, 65, 66, 67, 126, 127, 128, 129)]
+    ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), idx, qp, x["kv_len"].numpy(), 1, wl.scale,
+                             rows)
+    err = max(float(np.abs(got[s, i] - ref[s, i]).max()) for s, i in rows)
+    print(f"long token lists: max |O - oracle| {err:.2e} over {len(rows)} rows")
+    assert err <= 2e-2
+
+
 def test_attention_bf16_output_and_empty_rows():
     wl = inputs.mini(2)
     x = inputs.generate(wl)
