@@ -482,18 +482,23 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
 
   // the first two tiles
   __syncthreads();   // token ring filled
+  // All waves load the main parts (wave w: rows w, w + NW, ...), so that
+  // each issues half the loads (a load stalls the wave that issues it); the
+  // second group also loads the rope parts.
   int32_t g_tl = 0;   // token ids of the next tile to gather (second group)
-  if (grp == 1) {
+  {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     for (int u = 0; u < 2 && u < n_tiles; ++u) {
-      g_tl = tokens_of(u);
+      const int32_t tl = tokens_of(u);
 #pragma unroll
-      for (int k = 0; k < 32 / GW; ++k) gather_main(gl + GW * k, g_tl, kb_lds + u * KT_BYTES, ln);
+      for (int k = 0; k < 32 / NW; ++k) gather_main(wid + NW * k, tl, kb_lds + u * KT_BYTES, ln);
+      if (grp == 1) {
 #pragma unroll
-      for (int j = 0; j < N_ROPE; ++j) gather_rope(j, g_tl, kb_lds + u * KT_BYTES, ln);
+        for (int j = 0; j < N_ROPE; ++j) gather_rope(j, tl, kb_lds + u * KT_BYTES, ln);
+      }
     }
-    if (n_tiles > 2) g_tl = tokens_of(2);
+    if (grp == 1 && n_tiles > 2) g_tl = tokens_of(2);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
