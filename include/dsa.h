@@ -136,7 +136,8 @@ int dsa_index_scores(const dsa_index_desc* d, float* scores, void* stream);
  * For each query row: K = min(top_k / c, n_visible_units) units are kept:
  * first the forced sinks (units j < n_sink, token mode only: the sequence's
  * first keys), then the best remaining visible units by (score descending,
- * unit index ascending).  Writes idx [S, n_q, top_k / c] int32: the kept unit
+ * unit index ascending; scores compare as IEEE values, so -0 and +0 are
+ * equal and tie by index).  Writes idx [S, n_q, top_k / c] int32: the kept unit
  * ids in ascending order, then -1 for the dead slots.  A full argsort is never
  * formed.  Scores of invisible units are not read.
  * ---------------------------------------------------------------------- */
