@@ -93,6 +93,11 @@ __device__ uint32_t find_bin_desc(const uint32_t* hist, int nb, uint32_t need, u
 // run 16 t .. 16 t + 15, words 17 t + i) free of bank conflicts.
 __device__ __forceinline__ int64_t key_slot(int64_t e) { return e + (e >> 4); }
 
+// Histogram bins of the one-workgroup-per-row select: radix passes of
+// 11 + 11 + 10 bits, so that the histogram takes 8 KB of LDS and more rows
+// share a compute unit.
+constexpr int ROW_BINS = 1 << 11;
+
 // Keys e = tid, tid + 256, ... below m of a row into LDS.  Each thread issues
 // the loads of NB keys before converting any (in-range addresses only: past m
 // it reloads key m - 1), so a row of 4096 keys costs one memory latency
@@ -121,8 +126,8 @@ __device__ __forceinline__ void load_row_keys(const float* sc, int64_t m, uint32
 template <bool LONG>
 __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   extern __shared__ uint32_t s_mem[];
-  uint32_t* s_hist = s_mem;                 // HIST_BINS
-  uint32_t* s_scr = s_mem + HIST_BINS;      // 16
+  uint32_t* s_hist = s_mem;                 // ROW_BINS
+  uint32_t* s_scr = s_mem + ROW_BINS;       // 16
   uint32_t* s_key = s_scr + 16;             // row keys, padded (key_slot)
   const int64_t row = blockIdx.x;
   const RowInfo ri = row_info(p, row);
@@ -150,10 +155,10 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkParams p) {
   if (need0 == 0) return;   // every kept slot is a forced sink
   __syncthreads();
 
-  // radix select: 12 + 12 + 8 bits
+  // radix select: 11 + 11 + 10 bits
   uint32_t prefix = 0, pmask = 0, need = need0;
-  const int shifts[3] = {20, 8, 0};
-  const int nbits[3] = {12, 12, 8};
+  const int shifts[3] = {21, 10, 0};
+  const int nbits[3] = {11, 11, 10};
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int nb = 1 << nbits[pass], sh = shifts[pass];
@@ -528,7 +533,7 @@ hipError_t launch_topk_clear(const TopkParams& p, hipStream_t st) {
 hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   if (!topk_use_multiblock(rows, p.n_units)) {
-    const size_t lds = (HIST_BINS + 16 + static_cast<size_t>(p.n_units + p.n_units / 16 + 1)) * sizeof(uint32_t);
+    const size_t lds = (ROW_BINS + 16 + static_cast<size_t>(p.n_units + p.n_units / 16 + 1)) * sizeof(uint32_t);
     const bool long_rows = p.n_units > 2048;
     const void* fn = long_rows ? reinterpret_cast<const void*>(topk_row_kernel<true>)
                                : reinterpret_cast<const void*>(topk_row_kernel<false>);
