@@ -29,12 +29,14 @@ and notation of the pages:
   * the orthonormal Sylvester Walsh-Hadamard rotation of indexer q and k
     ((Hq).(Hk) = q.k, H symmetric with H.H = I: PR #2058 first and
     "kr_l maintenance" commits);
-  * the indexer-key cache write: new keys rotated in float32 and stored in the
-    cache type (f16, bf16, or fp8 e4m3fn with a per-row scale) at their cache
-    rows (PR #2058 "decode-correct indexer-K cache" commit; quantized indexer
-    and K caches in the ik_llama_opt log and unsloth llama.cpp PR #293).  This part
-    alone runs in float32, because its stored codes are integers that a
-    float decides (see its section).
+  * the indexer-key cache write: new keys rotated and stored in the cache
+    type (f16, bf16, or fp8 e4m3fn with a per-row scale) at their cache rows
+    (PR #2058 "decode-correct indexer-K cache" commit; quantized indexer and K
+    caches in the ik_llama_opt log and unsloth llama.cpp PR #293): the exact
+    rotated value rounded once into the type, plus the rule that says which
+    stored results a float32 rotation may validly produce (see its section);
+  * incremental re-pooling of persistent pooled keys (offgrid-sys
+    llama-memory-hybrid-idx.h).
 
 Where the pages leave a step open, the reading taken is stated at the function
 that takes it.  Every function is pinned by tests in tests/test_oracle.py
@@ -147,17 +149,6 @@ def visible_tokens(q_pos: int, kv_len: int) -> int:
     other).  q_pos < 0 sees nothing.
     """
     return max(0, min(q_pos + 1, kv_len))
-
-
-def complete_blocks(q_pos: int, kv_len: int, c: int) -> int:
-    """Number of complete blocks of c positions visible to a query.
-
-    Reading: a block [b*c, b*c + c) counts as complete for query i iff its last
-    position b*c + c - 1 is visible to i (<= q_pos and < kv_len).  Blocks are
-    cuts of the position line starting at the sequence's first position
-    (llama.cpp mirror commit c88c916636, fourth paragraph).
-    """
-    return visible_tokens(q_pos, kv_len) // c
 
 
 # --------------------------------------------------------------------------
@@ -294,6 +285,31 @@ def block_pool(k_raw: np.ndarray, c: int) -> np.ndarray:
     return out
 
 
+def block_pool_update(k_raw: np.ndarray, c: int, pooled: np.ndarray, from_block, kv_len=None) -> np.ndarray:
+    """Persistent pooled keys after one incremental re-pool.
+
+    The pooled keys live on across micro-batches: a micro-batch appends keys,
+    and only the pools it completes are computed; an edit of a sequence at
+    some position makes every pool from that position on stale
+    (offgrid-sys llama-memory-hybrid-idx.h: pooled keys persist in the index
+    cache across batches, the pools to re-pool per micro-batch, the stale
+    position of an edit).  For sequence s the blocks
+        max(from_block[s], 0) <= b < min(kv_len[s], n_kv) // c
+    are recomputed as the mean of their c raw rows (the blocks that are
+    complete in the stored keys); every other block keeps its value.
+    k_raw [S, n_kv, D], pooled [S, n_kv // c, D]; kv_len None = n_kv.
+    Returns the updated copy of `pooled`.
+    """
+    S, n_kv, D = k_raw.shape
+    out = np.array(pooled, dtype=np.float64, copy=True)
+    for s in range(S):
+        kl = n_kv if kv_len is None else min(int(kv_len[s]), n_kv)
+        b0 = max(int(from_block[s]), 0)
+        for b in range(b0, max(kl, 0) // c):
+            out[s, b] = np.asarray(k_raw[s, b * c:(b + 1) * c], dtype=np.float64).sum(axis=0) / c
+    return out
+
+
 def block_token_set(blocks: np.ndarray, c: int, q_pos: int, kv_len: int) -> np.ndarray:
     """Tokens attended by a query in block mode, in attention order.
 
@@ -413,59 +429,52 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, c: int, q_pos, kv_len=None,
 # at kv_head, and later read back whole for scoring; ik_llama_opt log,
 # "GLM-DSA: allow for quantized indexer cache"; unsloth llama.cpp PR #293
 # (deepseek41 quantized K cache): rows are rotated in F32 and then stored in
-# the cache type.  The cache types here are f16, bf16 and fp8 e4m3fn with one f32 scale
-# per row (the long-decode workload's format; not on the pages).
+# the cache type.  The cache types here are f16, bf16 and fp8 e4m3fn with one
+# f32 scale per row (the long-decode workload's format; not on the pages).
 #
-# Because a stored code is an integer decided by floating point, this part
-# computes in float32, the precision the pages name for the rotation, instead
-# of float64: the rotation is the fast Walsh-Hadamard transform (butterfly
-# spans 1, 2, 4, ..., 64, in that order, (a, b) -> (a + b, a - b)), then, for
-# 16-bit caches, a multiplication by float32(1/sqrt(128)); every step is one
-# correctly rounded float32 operation, so the result is fixed bit for bit.
-#
-# fp8 rows (the library's own format; the pages fix only that rows are rotated in
-# F32 before they are stored in the cache type): with y the row after the butterflies (not yet
-# normalised) and m = max |y|, code = e4m3fn(y * (448 / m)) and scale =
-# m * float32(1 / (448 sqrt(128))) (1 / 448 for an unrotated row), so that
-# code * scale is the normalised rotated value to within the fp8 rounding.
-# One division per row, none per element.
+# The oracle states the value the pages fix, exactly: the stored element is
+# the rotated key y = H x (H the orthonormal Sylvester matrix, computed in
+# float64 from the stored input values) rounded once into the cache type.
+#   * f16 / bf16 caches: nearest, ties to even.
+#   * fp8 caches: scale = max_d |y(d)| / 448 (so the largest element maps to
+#     +-448), code = e4m3fn(y(d) / scale), nearest with ties to the even code,
+#     saturating at 448; a zero row has scale 0 and zero codes.
+# An implementation that rotates in float32, as the pages do, cannot always
+# reach that rounding: its rotated value carries float32 rounding error, and
+# where the exact value lies within that error of a rounding midpoint of the
+# cache type it may round to the other neighbour.  key_write_check() states
+# which stored results are therefore valid.
 
 FP8_E4M3_MAX = 448.0
+F32_EPS = 2.0 ** -24        # unit roundoff of float32 (half an ulp of 1)
 
 
-def fwht_f32(x: np.ndarray) -> np.ndarray:
-    """Normalised Walsh-Hadamard transform of the last axis in float32.
+def round_to_format(v: np.ndarray, p: int, emin: int) -> np.ndarray:
+    """float64 values rounded once to a binary format with p significand bits
+    (implicit bit included) and minimum normal exponent emin: nearest, ties to
+    even, gradual underflow.  The exponent range above is assumed wide enough
+    (no overflow).  bf16: p = 8, emin = -126; f16: p = 11, emin = -14."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                    # v = m 2^e, 0.5 <= |m| < 1
+    ulp = np.ldexp(1.0, np.maximum(e - p, emin - p + 1))
+    return np.rint(v / ulp) * ulp         # np.rint rounds half to even
 
-    Equals hadamard(n) @ x up to float32 rounding; the butterfly order above
-    fixes the rounding.  The last axis must be a power of two.
-    """
-    y = butterflies_f32(x)
-    return y * np.float32(1.0 / math.sqrt(y.shape[-1]))
+
+def encode_f16_bits(v: np.ndarray) -> np.ndarray:
+    """float64 values -> IEEE binary16 bit patterns, rounded once (nearest,
+    ties to even)."""
+    return round_to_format(v, 11, -14).astype(np.float16).view(np.uint16)
 
 
-def butterflies_f32(x: np.ndarray) -> np.ndarray:
-    """The unnormalised fast Walsh-Hadamard transform of the last axis in
-    float32: sqrt(n) * hadamard(n) @ x up to float32 rounding."""
-    y = np.array(x, dtype=np.float32, copy=True)
-    n = y.shape[-1]
-    if n < 1 or n & (n - 1):
-        raise ValueError("transform length must be a power of two")
-    lead = y.shape[:-1]
-    h = 1
-    while h < n:
-        # last axis as (block, half, offset): element blk*2h + half*h + r
-        y = y.reshape(lead + (n // (2 * h), 2, h))
-        a = y[..., 0, :].copy()
-        b = y[..., 1, :].copy()
-        y[..., 0, :] = a + b
-        y[..., 1, :] = a - b
-        y = y.reshape(lead + (n,))
-        h *= 2
-    return y
+def encode_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float64 values -> bfloat16 bit patterns, rounded once (nearest, ties to
+    even).  The rounded value is exact in float32, whose upper half it is."""
+    r = round_to_format(v, 8, -126).astype(np.float32)
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
-    """float32 values -> OCP e4m3fn codes (uint8).
+    """Values (float32 or float64) -> OCP e4m3fn codes (uint8).
 
     The nearest finite e4m3fn value, ties to the even code (the code's last
     bit is the mantissa's last bit); magnitudes above 448 saturate to 448; the
@@ -473,7 +482,9 @@ def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
     0x80).  Written from the format's definition: the magnitude is compared
     with the table of the 127 non-negative finite values.
     """
-    v = np.asarray(v, dtype=np.float32)
+    v = np.asarray(v)
+    if v.dtype not in (np.float32, np.float64):
+        v = v.astype(np.float64)
     table = decode_fp8_e4m3fn(np.arange(127, dtype=np.uint8))   # codes 0..126, ascending values
     a = np.abs(v).astype(np.float64)
     hi = np.minimum(np.searchsorted(table, a, side="left"), 126)
@@ -486,37 +497,139 @@ def encode_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
     return (code | (sign << 7)).astype(np.uint8)
 
 
-def index_key_write(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool):
-    """Rows to store for new indexer keys [..., D] (exact float32 values).
-
-    cache_dtype 'f16' or 'bf16': returns the rotated (hadamard_k) or plain rows
-    rounded to nearest, ties to even, as uint16 bit patterns, and None.
-    'fp8': returns (codes uint8 [..., D], scale float32 [...]) as described
-    above the section; a row of zeros gets scale 0 and codes 0.  The rotation
-    needs D = 128.
-    """
-    x = np.asarray(k_new, dtype=np.float32)
-    if hadamard_k and x.shape[-1] != 128:
+def rotate_keys(k_new: np.ndarray, hadamard_k: bool) -> np.ndarray:
+    """The rotated keys y = H x of new indexer keys [..., D] in float64 (x
+    unchanged when hadamard_k is false).  The rotation needs D = 128."""
+    x = np.asarray(k_new, dtype=np.float64)
+    if not hadamard_k:
+        return x.copy()
+    if x.shape[-1] != 128:
         raise ValueError("the rotation is defined for 128-wide keys")
-    if cache_dtype in ("f16", "bf16"):
-        if hadamard_k:
-            x = fwht_f32(x)
-        if cache_dtype == "f16":
-            return x.astype(np.float16).view(np.uint16), None
-        import torch  # the library's float32 -> bfloat16 rounding (nearest, ties to even)
+    return x @ hadamard(128).T
 
-        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), None
+
+def index_key_write(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool):
+    """What the cache stores for new indexer keys [..., D] (exact values).
+
+    cache_dtype 'f16' or 'bf16': returns (bit patterns uint16 [..., D], None),
+    the rotated (hadamard_k) or plain rows rounded once to the type.
+    'fp8': returns (codes uint8 [..., D], scale float64 [...]): scale = max_d
+    |y(d)| / 448 exactly, codes = e4m3fn(y / scale); a zero row gets scale 0
+    and codes 0.
+    """
+    y = rotate_keys(k_new, hadamard_k)
+    if cache_dtype == "f16":
+        return encode_f16_bits(y), None
+    if cache_dtype == "bf16":
+        return encode_bf16_bits(y), None
     if cache_dtype != "fp8":
         raise ValueError(cache_dtype)
-    y = butterflies_f32(x) if hadamard_k else x
-    m = np.abs(y).max(axis=-1).astype(np.float32)
-    live = m > 0
-    inv = np.zeros_like(m)
-    np.divide(np.float32(FP8_E4M3_MAX), m, out=inv, where=live)
-    unit = np.float32(1.0 / (FP8_E4M3_MAX * math.sqrt(128.0))) if hadamard_k else np.float32(1.0 / FP8_E4M3_MAX)
-    scale = (m * unit).astype(np.float32)
-    q = (y * inv[..., None]).astype(np.float32)
+    scale = np.abs(y).max(axis=-1) / FP8_E4M3_MAX
+    live = scale > 0
+    q = np.zeros_like(y)
+    np.divide(y, scale[..., None], out=q, where=live[..., None])
     return encode_fp8_e4m3fn(q), scale
+
+
+def rotation_error_bound(k_new: np.ndarray, hadamard_k: bool) -> np.ndarray:
+    """Bound on the float32 rounding error of a rotated element, per row.
+
+    A float32 fast Walsh-Hadamard transform of 128 points runs 7 butterfly
+    stages (a, b) -> (a + b, a - b), each rounded once, then one product by
+    float32(1/sqrt(128)).  The nodes of one stage that an output depends on
+    cover disjoint sets of inputs, so the rounding errors of a stage add up to
+    at most u * sum_d |x(d)| (u = 2^-24), and the unnormalised output is off
+    by at most 7 u sum_d |x(d)|, i.e. 7 u sum_d |x(d)| / sqrt(128) after the
+    normalisation (whose own two roundings are relative, accounted for by the
+    caller).  Zero when the rows are not rotated."""
+    x = np.asarray(k_new, dtype=np.float64)
+    if not hadamard_k:
+        return np.zeros(x.shape[:-1])
+    return 7.0 * F32_EPS * np.abs(x).sum(axis=-1) / math.sqrt(128.0)
+
+
+def _neighbour_ok(got_val: np.ndarray, want_val: np.ndarray, exact: np.ndarray, mid_lo: np.ndarray,
+                  mid_hi: np.ndarray, delta: np.ndarray) -> np.ndarray:
+    """True where got equals want, or where got is the other neighbour of a
+    midpoint that the exact value lies within delta of."""
+    same = got_val == want_val
+    near_lo = (np.abs(exact - mid_lo) <= delta) & (got_val < want_val)
+    near_hi = (np.abs(exact - mid_hi) <= delta) & (got_val > want_val)
+    return same | near_lo | near_hi
+
+
+def _grid_neighbours(want_val: np.ndarray, step_down: np.ndarray, step_up: np.ndarray):
+    """Midpoints between a rounded value and its lower and upper neighbours."""
+    return want_val - step_down / 2.0, want_val + step_up / 2.0
+
+
+def key_write_check(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool, got, got_scale=None):
+    """Validity of stored key rows against the exact rotated values.
+
+    got: bit patterns (uint16, f16 / bf16) or codes (uint8, fp8) [..., D];
+    got_scale: [...] float32 row scales (fp8).  A stored element is valid when
+    it is the oracle's rounding of the exact value, or, where the exact value
+    lies within a float32 rotation's rounding error (rotation_error_bound plus
+    the relative error of the normalising and scaling products) of the
+    midpoint between two neighbours of the cache type, the other neighbour.
+    A stored fp8 scale is valid within the same relative error of the exact
+    max / 448.  Zero values compare equal whatever their sign.
+
+    Returns (ok, n_exceptions): ok is a boolean array [..., D] (and [...] for
+    the scales, folded in: a bad scale marks its whole row), n_exceptions the
+    number of valid elements that took the other neighbour.
+    """
+    y = rotate_keys(k_new, hadamard_k)
+    E = rotation_error_bound(k_new, hadamard_k)[..., None]   # absolute, on y
+    want, want_scale = index_key_write(k_new, cache_dtype, hadamard_k)
+    if cache_dtype in ("f16", "bf16"):
+        dec = decode_f16 if cache_dtype == "f16" else decode_bf16
+        p, emin = (11, -14) if cache_dtype == "f16" else (8, -126)
+        wv, gv = dec(want), dec(np.asarray(got))
+        # neighbour spacing of the rounded value: ulp below and above
+        _, e = np.frexp(wv)
+        ulp = np.ldexp(1.0, np.maximum(e - p, emin - p + 1))
+        is_pow2 = (np.frexp(np.abs(wv))[0] == 0.5) & (wv != 0)
+        down = np.where(is_pow2 & (np.abs(wv) > np.ldexp(1.0, emin)), ulp / 2.0, ulp)
+        lo_mid, hi_mid = _grid_neighbours(np.abs(wv), down, ulp)
+        delta = E + 3.0 * F32_EPS * np.abs(y)
+        ok = _neighbour_ok(np.abs(gv), np.abs(wv), np.abs(y), lo_mid, hi_mid, delta)
+        ok &= (np.sign(gv) == np.sign(wv)) | (gv == 0) | (wv == 0)
+        ok &= np.isfinite(gv)
+        exc = int(((gv != wv) & ok).sum())
+        return ok, exc
+    if cache_dtype != "fp8":
+        raise ValueError(cache_dtype)
+    m = np.abs(y).max(axis=-1)                               # exact row max
+    live = m > 0
+    got_scale = np.asarray(got_scale, dtype=np.float64)
+    # the scale: a float32 rotation's max is off by at most E, the scale
+    # product rounds twice (the constant and the product)
+    tol_s = (E[..., 0] + 3.0 * F32_EPS * m) / FP8_E4M3_MAX
+    ok_scale = np.where(live, np.abs(got_scale - want_scale) <= tol_s, got_scale == 0)
+    table = decode_fp8_e4m3fn(np.arange(127, dtype=np.uint8))
+    wv = np.abs(decode_fp8_e4m3fn(want))
+    gv = np.abs(decode_fp8_e4m3fn(np.asarray(got)))
+    v = np.zeros_like(y)
+    np.divide(np.abs(y), (m / FP8_E4M3_MAX)[..., None], out=v, where=live[..., None])
+    # the scaled value 448 y / m computed from a float32 rotation: each of y
+    # and m is off by at most E, and the reciprocal and the product round
+    # once each
+    mm = np.where(live, m, 1.0)[..., None]
+    delta = FP8_E4M3_MAX * 2.0 * E / np.maximum(mm - E, mm / 2) + 3.0 * F32_EPS * np.maximum(v, 1.0)
+    pos = np.searchsorted(table, wv)
+    lower = table[np.maximum(pos - 1, 0)]
+    upper = table[np.minimum(pos + 1, 126)]
+    lo_mid = (wv + lower) / 2.0
+    hi_mid = np.where(pos >= 126, np.inf, (wv + upper) / 2.0)
+    ok = _neighbour_ok(gv, wv, v, lo_mid, hi_mid, delta)
+    yy = np.where(live[..., None], y, 0.0)
+    gsign = np.signbit(decode_fp8_e4m3fn(np.asarray(got)))
+    ok &= (gsign == np.signbit(yy)) | (gv == 0) | (wv == 0)
+    ok &= np.isfinite(decode_fp8_e4m3fn(np.asarray(got)))
+    ok &= ok_scale[..., None]
+    exc = int(((gv != wv) & ok).sum())
+    return ok, exc
 
 
 # --------------------------------------------------------------------------

@@ -402,33 +402,53 @@ def test_attention_token_order_only_changes_rounding():
 
 # ------------------------------------------------------ indexer-key cache write --
 
-def test_fwht_f32_matches_the_hadamard_matrix():
-    # the fast butterflies compute the Sylvester matrix product (fp64 reference)
-    x = np.random.default_rng(11).standard_normal((64, 128)).astype(np.float32)
-    ref = x.astype(np.float64) @ O.hadamard(128)
-    got = O.fwht_f32(x)
-    assert got.dtype == np.float32
-    assert np.abs(got - ref).max() <= 1e-6 * np.abs(x).max() * math.sqrt(128)
+def test_rounding_to_16_bit_formats_is_single_and_to_even():
+    # f16: numpy's float64 -> float16 conversion is one correct rounding; bf16:
+    # torch's float32 -> bfloat16 cast is one on float32 inputs
+    g = np.random.default_rng(11)
+    v = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-6, 4, 20000),
+                        [0.0, -0.0, 2.0 ** -24, 2.0 ** -25 * 3, 65504.0, -1.0]])
+    assert np.array_equal(O.encode_f16_bits(v), v.astype(np.float16).view(np.uint16))
+    v32 = v.astype(np.float32)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.encode_bf16_bits(v32.astype(np.float64)), ref)
+    # a value just above a bf16 midpoint by less than float32 resolution
+    # rounds up (rounding through float32 first would tie and go to the even 1.0)
+    assert O.decode_bf16(O.encode_bf16_bits(np.array([1 + 2.0 ** -8 + 2.0 ** -40])))[0] == 1 + 2.0 ** -7
+    # exact midpoints tie to the even neighbour
+    assert O.decode_bf16(O.encode_bf16_bits(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]))).tolist() == [1.0, 1 + 2 * 2.0 ** -7]
+    # 1/sqrt(128) = 1.41421356... * 2^-4: the 8-bit significand 181/128 (bf16
+    # 0x3DB5), the 11-bit significand 1448/1024 (f16 0x2DA8), worked by hand
+    c = np.array([1 / math.sqrt(128)])
+    assert O.encode_bf16_bits(c)[0] == 0x3DB5 and O.encode_f16_bits(c)[0] == 0x2DA8
 
 
-def test_fwht_f32_of_basis_vectors_is_exact():
-    # H e_j is column j of H: entries +-1/sqrt(128), exact after the float32 scaling
-    eye = np.eye(128, dtype=np.float32)
-    got = O.fwht_f32(eye)
-    c = np.float32(1.0 / math.sqrt(128.0))
-    sign = np.sign(O.hadamard(128) * math.sqrt(128)).astype(np.float32)
-    assert np.array_equal(got, sign * c)
+def test_key_write_16bit_of_basis_vectors():
+    # H e_j is column j of H: entries +-1/sqrt(128), so every stored element is
+    # +-0x3DB5 (bf16) or +-0x2DA8 (f16) with the sign pattern of the Sylvester matrix
+    eye = np.eye(128)
+    sign = O.hadamard(128) * math.sqrt(128)
+    for name, mag in (("bf16", 0x3DB5), ("f16", 0x2DA8)):
+        bits, none = O.index_key_write(eye, name, True)
+        assert none is None
+        want = np.where(sign.T > 0, mag, mag | 0x8000)
+        assert np.array_equal(bits, want.astype(np.uint16))
+        plain, _ = O.index_key_write(eye, name, False)   # unrotated: 1.0 and 0.0
+        one = 0x3F80 if name == "bf16" else 0x3C00
+        assert np.array_equal(plain, (np.eye(128) * one).astype(np.uint16))
 
 
-def test_butterflies_are_the_unnormalised_transform():
-    x = np.random.default_rng(16).standard_normal((8, 128)).astype(np.float32)
-    assert np.abs(O.butterflies_f32(x) - math.sqrt(128) * (x.astype(np.float64) @ O.hadamard(128))).max() < 1e-4
-
-
-def test_fwht_f32_twice_is_identity():
-    # H is symmetric and orthonormal: H.H = I (pages: un-rotation is a second rotation)
-    x = np.random.default_rng(12).standard_normal((16, 128)).astype(np.float32)
-    assert np.abs(O.fwht_f32(O.fwht_f32(x)) - x).max() < 1e-5
+def test_key_write_rotation_is_the_sylvester_product():
+    # rotating twice gives the keys back (H.H = I), and a rotated query scores the
+    # stored rotated keys like the plain ones (to the storage precision)
+    g = np.random.default_rng(12)
+    k = g.standard_normal((16, 128))
+    assert np.abs(O.rotate_keys(O.rotate_keys(k, True), True) - k).max() < 1e-12
+    assert np.array_equal(O.rotate_keys(k, False), k)
+    bits16, _ = O.index_key_write(k, "f16", True)
+    q = g.standard_normal((3, 128))
+    d_rot = (q @ O.hadamard(128)) @ O.decode_f16(bits16).T
+    assert np.abs(d_rot - q @ k.T).max() < 2e-2
 
 
 def test_fp8_encode_matches_torch_in_range():
@@ -454,41 +474,122 @@ def test_fp8_encode_round_trip_and_saturation():
     assert O.encode_fp8_e4m3fn(np.float32(1.1875))[()] == 0x3A   # between 0x39 and 0x3A: even wins
 
 
+def test_key_write_fp8_closed_forms():
+    # x = e_0: H x = 1/sqrt(128) in every element, so scale = (1/sqrt(128)) / 448
+    # and every code is 448 (0x7E); x = e_0 - e_1: H x is 0 on even and
+    # 2/sqrt(128) on odd elements (Sylvester order), so codes 0 and 448
+    k = np.zeros((3, 128))
+    k[0, 0] = 1.0
+    k[1, 0], k[1, 1] = 1.0, -1.0
+    codes, scale = O.index_key_write(k, "fp8", True)
+    assert scale[0] == (1 / math.sqrt(128)) / 448 and np.all(codes[0] == 0x7E)
+    assert scale[1] == (2 / math.sqrt(128)) / 448
+    assert np.all(codes[1, 0::2] == 0) and np.all(codes[1, 1::2] == 0x7E)
+    assert scale[2] == 0 and not codes[2].any()       # a zero row: scale 0, zero codes
+    # unrotated: the scale is the row's max / 448 and that element stores +-448
+    k2 = np.array([[3.0, -6.0] + [0.5] * 126])
+    c2, s2 = O.index_key_write(k2, "fp8", False)
+    assert s2[0] == 6.0 / 448 and c2[0, 1] == 0xFE and c2[0, 0] == O.encode_fp8_e4m3fn(np.array([224.0]))[0]
+
+
 def test_key_write_fp8_bounds_and_extremes():
     g = np.random.default_rng(14)
-    k = g.standard_normal((40, 128)).astype(np.float32)
+    k = g.standard_normal((40, 128)).astype(np.float32).astype(np.float64)
     k[3] *= 8.0
     k[5] = 0.0
     for rot in (False, True):
         codes, scale = O.index_key_write(k, "fp8", rot)
-        x = O.fwht_f32(k) if rot else k
-        assert scale.dtype == np.float32 and codes.dtype == np.uint8
-        assert scale[5] == 0 and not codes[5].any()
+        y = k @ O.hadamard(128).T if rot else k
+        assert codes.dtype == np.uint8 and scale[5] == 0 and not codes[5].any()
         live = np.arange(40) != 5
+        assert np.allclose(scale[live], np.abs(y[live]).max(-1) / 448, rtol=1e-15, atol=0)
         # the largest magnitude of each row is stored as +-448
-        arg = np.abs(x[live]).argmax(-1)
+        arg = np.abs(y[live]).argmax(-1)
         assert np.all((codes[live][np.arange(39), arg] & 0x7F) == 0x7E)
-        # half-ulp bound of 3 mantissa bits (absolute 2^-10 in the subnormal range), in scale units
-        dec = O.decode_fp8_e4m3fn(codes) * scale[:, None].astype(np.float64)
-        q = x.astype(np.float64) / np.where(scale > 0, scale, 1)[:, None]
-        # plus the float32 roundings of the multiplier, the scale and the product
-        bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) * scale[:, None] + 1e-6 * np.abs(x)
-        assert np.all(np.abs(dec - x) <= bound)
+        # half a step of 3 mantissa bits (2^-10 absolute in the subnormal range), in scale units
+        dec = O.decode_fp8_e4m3fn(codes) * scale[:, None]
+        q = y / np.where(scale > 0, scale, 1)[:, None]
+        bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) * scale[:, None] * (1 + 1e-12)
+        assert np.all(np.abs(dec - y) <= bound)
 
 
-def test_key_write_16bit_rows_and_rotation_invariance():
+def test_key_write_check_accepts_the_oracle_and_rejects_plants():
     g = np.random.default_rng(15)
-    k = g.standard_normal((8, 128)).astype(np.float32)
-    q = g.standard_normal((3, 128))
-    bits16, none = O.index_key_write(k, "f16", True)
-    assert none is None
-    assert np.array_equal(bits16, O.fwht_f32(k).astype(np.float16).view(np.uint16))
-    # scoring rotated q against the stored rotated keys recovers q . k (f16 storage precision)
-    stored = O.decode_f16(bits16)
-    d_rot = (q @ O.hadamard(128)) @ stored.T
-    assert np.abs(d_rot - q @ k.T.astype(np.float64)).max() < 2e-2
-    bb, _ = O.index_key_write(k, "bf16", False)
-    assert np.abs(O.decode_bf16(bb) - k).max() <= 2.0 ** -8 * np.abs(k).max()
+    k = g.standard_normal((24, 128)).astype(np.float32).astype(np.float64)
+    k[2] *= 8.0
+    k[4] = 0.0
+    for name in ("f16", "bf16", "fp8"):
+        for rot in (False, True):
+            got, sc = O.index_key_write(k, name, rot)
+            ok, exc = O.key_write_check(k, name, rot, got, None if sc is None else sc.astype(np.float32))
+            assert ok.all() and exc == 0
+            # one step off, on an element far from a rounding midpoint: rejected
+            bad = got.copy()
+            bad[7, 9] = bad[7, 9] + 1   # the next code / bit pattern up in magnitude
+            ok2, _ = O.key_write_check(k, name, rot, bad, None if sc is None else sc.astype(np.float32))
+            assert not ok2[7, 9] and ok2.sum() == ok2.size - 1
+    # a scale off by more than the rounding bound marks its row
+    got, sc = O.index_key_write(k, "fp8", True)
+    sc2 = sc.astype(np.float32).copy()
+    sc2[1] *= np.float32(1 + 2.0 ** -10)
+    ok3, _ = O.key_write_check(k, "fp8", True, got, sc2)
+    assert not ok3[1].any() and ok3[0].all()
+
+
+def test_key_write_check_allows_the_other_neighbour_only_at_a_midpoint():
+    # unrotated rows whose max is 448 put the values straight on the e4m3 grid:
+    # an element at the exact midpoint 1.0625 of codes 0x38 (1.0) and 0x39
+    # (1.125) rounds to the even 0x38, and 0x39 is valid too (a float32 path may
+    # land on either side); at 1.04, far from any midpoint, only 0x38 is
+    k = np.zeros((1, 128))
+    k[0, 0], k[0, 1], k[0, 2] = 448.0, 1.0625, 1.04
+    codes, sc = O.index_key_write(k, "fp8", False)
+    assert codes[0, 1] == 0x38 and codes[0, 2] == 0x38
+    alt = codes.copy()
+    alt[0, 1] = 0x39
+    ok, exc = O.key_write_check(k, "fp8", False, alt, sc.astype(np.float32))
+    assert ok.all() and exc == 1
+    alt[0, 2] = 0x39
+    ok, _ = O.key_write_check(k, "fp8", False, alt, sc.astype(np.float32))
+    assert not ok[0, 2]
+    # the same for a bf16 row: 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7
+    k16 = np.array([[1 + 2.0 ** -8, 1 + 2.0 ** -9] + [0.0] * 126])
+    bits, _ = O.index_key_write(k16, "bf16", False)
+    assert bits[0, 0] == 0x3F80 and bits[0, 1] == 0x3F80
+    b2 = bits.copy()
+    b2[0, 0] = 0x3F81
+    ok, exc = O.key_write_check(k16, "bf16", False, b2)
+    assert ok.all() and exc == 1
+    b2[0, 1] = 0x3F81
+    ok, _ = O.key_write_check(k16, "bf16", False, b2)
+    assert not ok[0, 1]
+
+
+# ------------------------------------------------------ incremental block pooling --
+
+def test_block_pool_update_equals_one_shot_after_micro_batches_and_an_edit():
+    # micro-batches pool only what they complete; the result equals a one-shot
+    # pool of the final keys, and blocks no update reached keep their value
+    g = np.random.default_rng(31)
+    S, n, D, c = 2, 100, 8, 8
+    k = g.standard_normal((S, n, D))
+    sentinel = np.full((S, n // c, D), -7.0)
+    p = O.block_pool_update(k, c, sentinel, [0, 0], kv_len=[30, 0])
+    assert np.allclose(p[0, :3], O.block_pool(k[:, :24], c)[0])   # 30 stored keys: 3 complete blocks
+    assert np.all(p[0, 3:] == -7.0) and np.all(p[1] == -7.0)
+    p = O.block_pool_update(k, c, p, [3, 0], kv_len=[100, 57])
+    full = O.block_pool(k, c)
+    assert np.allclose(p[0], full[0], rtol=0, atol=1e-15)
+    assert np.allclose(p[1, :7], full[1, :7]) and np.all(p[1, 7:] == -7.0)
+    # an edit of sequence 0 from position 41 stales its pools from block 5 on
+    k2 = k.copy()
+    k2[0, 41:] += 1.0
+    p2 = O.block_pool_update(k2, c, p, [41 // c, 99], kv_len=[100, 57])
+    assert np.array_equal(p2[0, :5], p[0, :5]) and np.allclose(p2[0, 5:], O.block_pool(k2, c)[0, 5:])
+    assert np.array_equal(p2[1], p[1])
+    # a constant block pools to its constant; a negative first block counts as 0
+    kc = np.full((1, 16, 4), 2.5)
+    assert np.all(O.block_pool_update(kc, 8, np.zeros((1, 2, 4)), [-3]) == 2.5)
 
 
 # ------------------------------------------------------------------ IndexShare --
