@@ -3,17 +3,19 @@
 One step = one dsa_forward call over the whole batch of the workload: indexer
 scores -> top-k -> sparse attention (block pooling first in block mode).
 Inputs are seeded synthetic tensors already resident in HBM.  Prints one JSON
-line.  The default workload is the 4096-token DSA prefill (128-head MLA
-attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048).
+line.  The headline workload is the 4096-token DSA prefill (128-head MLA
+attention over a 576-wide latent, 64-head bf16 indexer, top_k 2048); the
+line's "configs" object times the other four workloads with the same
+protocol (tiny prefill, batched decode, block-pooled chunk, long decode).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1..5]
                     [--no-cpu-baseline] [--no-next-rows] [--next-rows-only] [--no-flush]
-                    [--calib-copy]
+                    [--headline-only] [--calib-copy]
 
-Beside the hot path it times the indexer-key cache write (rotate + fp8
-quantise) at the long-decode cache shape, the incremental block pooling of
-one micro-batch, and an 8-layer IndexShare decode stack, reported under
-"next_rows".
+--config n makes workload n the headline and times nothing else.  Beside the
+hot path it times the indexer-key cache write (rotate + fp8 quantise) at the
+long-decode cache shape, the incremental block pooling of one micro-batch,
+and an 8-layer IndexShare decode stack, reported under "next_rows".
 """
 
 import argparse
@@ -23,7 +25,13 @@ import os
 import sys
 import time
 
-import numpy as np
+# The oracle's BLAS pool: every host core the run may use, set before numpy
+# loads its BLAS (an explicit OMP_NUM_THREADS, as on a shared host, is kept).
+_BLAS_THREADS = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count() or 1)
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, _BLAS_THREADS)
+
+import numpy as np  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -31,7 +39,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 CSRC = os.path.join(ROOT, "sparse_top_attention_indexer_amd")
 PROFILES = os.path.join(ROOT, "profiles")
-PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+# dense MFMA peaks; f32 is the vector (VALU) peak of code built without
+# packed-FP32 instructions: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "fp8": 5.0e15, "f32": 78.6e12}
 
 
 def parse():
@@ -39,7 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: DSA prefill)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only workload 1..5 as the headline (default: workload 2, plus the others)")
+    ap.add_argument("--headline-only", action="store_true", help="do not time the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not evict the caches before each timed step (warm-cache timing by wall clock)")
@@ -193,7 +205,8 @@ def cpu_baseline(wl, x, budget_s):
     except OSError:
         pass
     return {"value": done / t_total, "unit": "query tokens/s", "keys_scored_per_s": scored / t_total,
-            "cores": threads, "cpu_model": model, "kind": "oracle",
+            "cores": threads, "host_cores": os.cpu_count(), "blas_threads": threads,
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{done} of {len(rows)} query rows of the {wl.name} batch, taken in bit-reversed order "
                       f"(evenly spread), numpy float64 oracle, {t_total:.1f} s"}
 
@@ -320,6 +333,119 @@ def index_share_row(dsa, inputs, torch, steps):
 
 # ---------------------------------------------------------------------- main
 
+def time_workload(dsa, inputs, torch, wl, steps, warmup, flush):
+    """Times `steps` dsa_forward steps of workload wl (after `warmup` untimed
+    ones), with the caches flushed before each timed step unless flush is
+    None.  Returns (result dict, inputs)."""
+    dev = "cuda"
+    x = inputs.generate(wl, device=dev)
+    kw = dict(k_scale=x["k_scale"], n_sink=wl.n_sink if wl.c == 1 else 0, scale=wl.scale,
+              hadamard_q=wl.hadamard_q, kv_len=x["kv_len"])
+    out = torch.empty((wl.S, wl.n_q, wl.Hq, wl.Dv), device=dev, dtype=torch.float32)
+    nbytes = dsa.forward_workspace_bytes(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k,
+                                         wl.c, x["q_pos"], **kw)
+    ws = torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
+    ev = [[dsa.Event() for _ in range(5)] for _ in range(steps)]
+
+    def step(events=None):
+        dsa.forward(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k, wl.c, x["q_pos"],
+                    out=out, workspace=ws, phase_events=events, **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if flush is not None:
+            flush.amax()
+        step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = sorted(ev[k][0].elapsed_ms(ev[k][4]) for k in range(steps))
+    ms_step = sum(step_ms) / steps if flush is not None else elapsed * 1e3 / steps
+    warm_ms = None
+    if flush is not None:   # the same steps back to back with warm caches, labelled as such
+        n_warm = max(1, min(steps, 10))
+        ew = [dsa.Event() for _ in range(2)]
+        ew[0].record()
+        for _ in range(n_warm):
+            step()
+        ew[1].record()
+        torch.cuda.synchronize()
+        warm_ms = ew[0].elapsed_ms(ew[1]) / n_warm
+
+    # per-phase times from the HIP events recorded on the library's stream
+    names = ["scores", "topk", "attn", "combine"]
+    phase_ms = {n_: 0.0 for n_ in names}
+    for k in range(steps):
+        for j, n_ in enumerate(names):
+            phase_ms[n_] += ev[k][j].elapsed_ms(ev[k][j + 1]) / steps
+
+    work, pairs_score, pairs_attn = work_model(wl, x["q_pos"].cpu().numpy(), x["kv_len"].cpu().numpy())
+    if wl.c > 1:   # pooling runs inside the first phase with the scores
+        work["scores"] = {"flops": work["scores"]["flops"], "bytes": work["scores"]["bytes"] + work["pool"]["bytes"]}
+    # the split merge runs in the attention phase's second launch: its time counts with attention
+    phase_ms_attn = phase_ms["attn"] + phase_ms["combine"]
+    cdt = compute_dtype(wl)
+    per_phase = {}
+    for n_ in ("scores", "topk", "attn"):
+        t = max((phase_ms_attn if n_ == "attn" else phase_ms[n_]) * 1e-3, 1e-12)
+        fl, by = work[n_]["flops"], work[n_]["bytes"]
+        peak_f = PEAK["f16" if (n_ == "scores" and wl.k_dtype != torch.bfloat16 and cdt != "f32") else cdt]
+        if n_ == "scores" and cdt == "f32":
+            peak_f = PEAK["f32"]
+        t_f, t_b = fl / peak_f, by / PEAK_HBM
+        bound = "mfma" if t_f >= t_b else "hbm"
+        if cdt == "f32" and bound == "mfma":
+            bound = "alu"
+        per_phase[n_] = dict(ms=t * 1e3, flops=fl, bytes=by, bound=bound,
+                             frac=(t_f if bound != "hbm" else t_b) / t, peak=peak_f if bound != "hbm" else PEAK_HBM)
+    # the dominant kernel: the longest single launch (attention without its merge)
+    launch_ms = {"scores": phase_ms["scores"], "topk": phase_ms["topk"], "attn": phase_ms["attn"]}
+    dom = max(launch_ms, key=lambda n_: launch_ms[n_])
+    ph = per_phase[dom]
+    t_dom = launch_ms[dom] * 1e-3
+    if ph["bound"] in ("mfma", "alu"):
+        roof = {"bound": ph["bound"], "achieved": ph["flops"] / t_dom / 1e12, "peak": ph["peak"] / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": ph["bytes"] / t_dom / 1e9, "peak": ph["peak"] / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = {"scores": score_kernel_name(wl), "topk": "topk kernels", "attn":
+                      {"mla": "attn_mla_kernel", "gqa": "attn_gqa_kernel", "f32": "attn_f32_kernel"}[wl.attn]}[dom]
+    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
+    roof["launch_ms"] = launch_ms[dom]
+    step_bytes = sum(work[n_]["bytes"] for n_ in ("scores", "topk", "attn"))
+    res = {
+        "workload": wl.name,
+        "query_tokens_per_s": wl.S * wl.n_q / (ms_step * 1e-3),
+        "keys_scored_per_s": pairs_score / (ms_step * 1e-3),
+        "keys_scored_per_s_score_phase": pairs_score / max(phase_ms["scores"] * 1e-3, 1e-12),
+        "ms_per_step": ms_step,
+        "config": {"workload": wl.name, "sequences": wl.S, "queries_per_sequence": wl.n_q, "cached_keys": wl.n_kv,
+                   "indexer_heads": wl.H, "indexer_dim": wl.D, "indexer_key_dtype": str(wl.k_dtype).split(".")[1],
+                   "top_k": wl.top_k, "compress_ratio": wl.c, "n_sink": wl.n_sink, "attention": wl.attn,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "dk": wl.Dk, "dv": wl.Dv,
+                   "scored_pairs": pairs_score, "attended_pairs": pairs_attn},
+        "dtype": cdt,
+        "timing": {"cache": "flushed before each step (1 GiB read)" if flush is not None else "warm",
+                   "steps": steps, "warmup": warmup,
+                   "step_ms_median": round(step_ms[len(step_ms) // 2], 5),
+                   "step_ms_p10": round(step_ms[int(0.1 * (len(step_ms) - 1))], 5),
+                   "step_ms_p90": round(step_ms[int(0.9 * (len(step_ms) - 1))], 5),
+                   "wall_ms_per_step": round(elapsed * 1e3 / steps, 5),
+                   "warm_cache_ms_per_step": None if warm_ms is None else round(warm_ms, 5),
+                   "step_clock": "HIP events around each step" if flush is not None else "wall clock"},
+        "phases_ms": {k_: round(v_, 5) for k_, v_ in phase_ms.items()},
+        "phase_roofline": {k_: {"bound": v_["bound"], "frac": round(v_["frac"], 4)} for k_, v_ in per_phase.items()},
+        # the whole step's algorithmic HBM bytes over its time (the decode workloads' bound)
+        "step_hbm": {"bytes": step_bytes, "achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac_of_8TBps": step_bytes / (ms_step * 1e-3) / PEAK_HBM},
+        "roofline": roof,
+    }
+    return res, x
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,123 +461,59 @@ def main():
                                         "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
                                         "index_share": index_share_row(dsa, inputs, torch, 5)}}), flush=True)
         return
-    wl = inputs.preset(args.config)
-    dev = "cuda"
-    x = inputs.generate(wl, device=dev)
-    kw = dict(k_scale=x["k_scale"], n_sink=wl.n_sink if wl.c == 1 else 0, scale=wl.scale,
-              hadamard_q=wl.hadamard_q, kv_len=x["kv_len"])
-    out = torch.empty((wl.S, wl.n_q, wl.Hq, wl.Dv), device=dev, dtype=torch.float32)
-    nbytes = dsa.forward_workspace_bytes(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k,
-                                         wl.c, x["q_pos"], **kw)
-    ws = torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
-    ev = [[dsa.Event() for _ in range(5)] for _ in range(args.steps)]
-
-    def step(events=None):
-        dsa.forward(x["Q"], x["K"], x["V"], x["q_idx"], x["k_idx"], x["w"], wl.top_k, wl.c, x["q_pos"],
-                    out=out, workspace=ws, phase_events=events, **kw)
-
+    headline = args.config if args.config is not None else 2
     # Before each timed step a 1 GiB read evicts the L2s and the 256 MB
     # Infinity Cache, so that a step finds its inputs in HBM, as it would
     # after the other layers of a model ran.  A read leaves clean lines (a
     # write would leave dirty ones for the step to write back).  The flush
     # runs before the step's first library event, never inside the step.
-    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        if flush is not None:
-            flush.amax()
-        step(ev[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    step_ms = sorted(ev[k][0].elapsed_ms(ev[k][4]) for k in range(args.steps))
-    ms_step = sum(step_ms) / args.steps if flush is not None else elapsed * 1e3 / args.steps
-    warm_ms = None
-    if flush is not None:   # the same steps back to back with warm caches, labelled as such
-        n_warm = max(1, min(args.steps, 10))
-        ew = [dsa.Event() for _ in range(2)]
-        ew[0].record()
-        for _ in range(n_warm):
-            step()
-        ew[1].record()
-        torch.cuda.synchronize()
-        warm_ms = ew[0].elapsed_ms(ew[1]) / n_warm
-
-    # per-phase times from the HIP events recorded on the library's stream
-    names = ["scores", "topk", "attn", "combine"]
-    phase_ms = {n_: 0.0 for n_ in names}
-    for k in range(args.steps):
-        for j, n_ in enumerate(names):
-            phase_ms[n_] += ev[k][j].elapsed_ms(ev[k][j + 1]) / args.steps
-
-    work, pairs_score, pairs_attn = work_model(wl, x["q_pos"].cpu().numpy(), x["kv_len"].cpu().numpy())
-    if wl.c > 1:   # pooling runs inside the first phase with the scores
-        work["scores"] = {"flops": work["scores"]["flops"], "bytes": work["scores"]["bytes"] + work["pool"]["bytes"]}
-    cdt = compute_dtype(wl)
-    per_phase = {}
-    for n_ in ("scores", "topk", "attn"):
-        t = max(phase_ms[n_] * 1e-3, 1e-12)
-        fl, by = work[n_]["flops"], work[n_]["bytes"]
-        peak_f = PEAK["f16" if (n_ == "scores" and wl.k_dtype != torch.bfloat16 and cdt != "f32") else cdt]
-        if n_ == "scores" and cdt == "f32":
-            peak_f = PEAK["f32"]
-        t_f, t_b = fl / peak_f, by / PEAK_HBM
-        bound = "mfma" if t_f >= t_b else "hbm"
-        per_phase[n_] = dict(ms=phase_ms[n_], flops=fl, bytes=by, bound=bound,
-                             frac=(t_f if bound == "mfma" else t_b) / t, peak=peak_f if bound == "mfma" else PEAK_HBM)
-    dom = max(("scores", "topk", "attn"), key=lambda n_: phase_ms[n_])
-    ph = per_phase[dom]
-    t_dom = ph["ms"] * 1e-3
-    if ph["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": ph["flops"] / t_dom / 1e12, "peak": ph["peak"] / 1e12,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": ph["bytes"] / t_dom / 1e9, "peak": ph["peak"] / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = {"scores": score_kernel_name(wl), "topk": "topk kernels", "attn":
-                      {"mla": "attn_mla_kernel", "gqa": "attn_gqa_kernel", "f32": "attn_f32_kernel"}[wl.attn]}[dom]
-    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
-    roof["launch_ms"] = ph["ms"]
-
-    q_tokens = wl.S * wl.n_q
-    value = q_tokens / (ms_step * 1e-3)
+    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    wl = inputs.preset(headline)
+    res, x = time_workload(dsa, inputs, torch, wl, args.steps, args.warmup, flush)
     line = {
         "metric": "query tokens/s + indexer keys scored/s (1 GPU), % of MFMA/HBM roofline",
-        "value": value,
+        "value": res["query_tokens_per_s"],
         "unit": "query tokens/s",
-        "keys_scored_per_s": pairs_score / (ms_step * 1e-3),
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cdt, "data": "synthetic",
-        "config": {"workload": wl.name, "sequences": wl.S, "queries_per_sequence": wl.n_q, "cached_keys": wl.n_kv,
-                   "indexer_heads": wl.H, "indexer_dim": wl.D, "indexer_key_dtype": str(wl.k_dtype).split(".")[1],
-                   "top_k": wl.top_k, "compress_ratio": wl.c, "n_sink": wl.n_sink, "attention": wl.attn,
-                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "dk": wl.Dk, "dv": wl.Dv,
-                   "scored_pairs": pairs_score, "attended_pairs": pairs_attn},
-        "timing": {"cache": "flushed before each step (1 GiB read)" if flush is not None else "warm",
-                   "step_ms_median": round(step_ms[len(step_ms) // 2], 5),
-                   "step_ms_p10": round(step_ms[int(0.1 * (len(step_ms) - 1))], 5),
-                   "step_ms_p90": round(step_ms[int(0.9 * (len(step_ms) - 1))], 5),
-                   "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 5),
-                   "warm_cache_ms_per_step": None if warm_ms is None else round(warm_ms, 5),
-                   "step_clock": "HIP events around each step" if flush is not None else "wall clock"},
-        "phases_ms": {k_: round(v_, 5) for k_, v_ in phase_ms.items()},
-        "phase_roofline_frac": {k_: round(v_["frac"], 4) for k_, v_ in per_phase.items()},
-        "roofline": roof,
+        "keys_scored_per_s": res["keys_scored_per_s"],
+        "keys_scored_per_s_score_phase": res["keys_scored_per_s_score_phase"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
+        "data": "synthetic",
+        "config": res["config"],
+        "timing": res["timing"],
+        "phases_ms": res["phases_ms"],
+        "phase_roofline": res["phase_roofline"],
+        "step_hbm": res["step_hbm"],
+        "roofline": res["roofline"],
     }
+    print(f"bench: workload {wl.name} done, {res['ms_per_step']:.4f} ms per step", file=sys.stderr, flush=True)
+    if args.config is None and not args.headline_only:
+        # the other workloads, same protocol, fewer steps; inputs freed in turn
+        others = {}
+        for n in (1, 3, 4, 5):
+            wl_n = inputs.preset(n)
+            r, xn = time_workload(dsa, inputs, torch, wl_n, min(args.steps, 10), min(args.warmup, 3), flush)
+            del xn
+            torch.cuda.empty_cache()
+            others[wl_n.name] = {k_: r[k_] for k_ in ("query_tokens_per_s", "keys_scored_per_s",
+                                                       "keys_scored_per_s_score_phase", "ms_per_step", "dtype",
+                                                       "timing", "phases_ms", "phase_roofline", "step_hbm",
+                                                       "roofline")}
+            print(f"bench: workload {wl_n.name} done, {r['ms_per_step']:.4f} ms per step", file=sys.stderr,
+                  flush=True)
+        line["configs"] = others
     if not args.no_next_rows:
         line["next_rows"] = {"index_key_write": key_write_row(dsa, inputs, torch, 20),
                              "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
                              "index_share": index_share_row(dsa, inputs, torch, 5)}
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
-        if args.config in (1, 3):   # the small and the batched-decode workloads also on one core
+        if headline in (1, 3):   # the small and the batched-decode workloads also on one core
             from threadpoolctl import threadpool_limits
             with threadpool_limits(limits=1):
                 one = cpu_baseline(wl, x, args.cpu_seconds / 2)

@@ -1070,23 +1070,17 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   hipError_t e;
   if (p.family == ATTN_MLA) {
-    static bool attr = false;
-    if (!attr) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mla_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_LDS));
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+    // set on every call (the same value each time, no state kept between calls)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mla_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_LDS));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_mla_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hq + 127) / 128),
                        dim3(64 * MLA_WAVES), MLA_LDS, st, p);
   } else if (p.family == ATTN_GQA) {
-    static bool attr = false;
-    if (!attr) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(4 * 2 * GQA_VT + 64 + MAX_BLOCKS * 4));
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+    // the largest size any call uses, so that concurrent calls set the same value
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(2 * GQA_VT + 64 + MAX_BLOCKS * 4));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_gqa_kernel, dim3(static_cast<unsigned>(gqa_grid(p))), dim3(64), gqa_lds_bytes(p), st,
                        p);
   } else {

@@ -752,17 +752,14 @@ static bool scores_use_stream(const ScoreParams& p) {
 template <int KK, int QK, int NQ>
 static hipError_t launch_stream_rb(const ScoreParams& p, dim3 grid, hipStream_t st) {
   const size_t lds = stream_lds_bytes<KK>(p.chunk_tiles);
-  static bool attr = false;
-  if (!attr) {
-    const int mx = static_cast<int>(stream_lds_bytes<KK>(32));
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 1, NQ>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 2, NQ>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the kernel's dynamic LDS limit, set on every call to the largest size any
+  // call uses (the same value each time: no state kept between calls, and
+  // concurrent calls agree)
+  const void* fn = p.H <= 32 ? reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 1, NQ>)
+                             : reinterpret_cast<const void*>(score_stream_kernel<KK, QK, 2, NQ>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(stream_lds_bytes<KK>(SC_MAX_TILES)));
+  if (e != hipSuccess) return e;
   if (p.H <= 32)
     hipLaunchKernelGGL((score_stream_kernel<KK, QK, 1, NQ>), grid, dim3(256), lds, st, p);
   else

@@ -12,9 +12,12 @@
 // finds the threshold key T and how many units equal to T are kept (the
 // lowest-indexed ones); an ordered compaction then writes the kept indices in
 // ascending order.
-//   - short rows (<= 16384 units, or many rows): one workgroup per row, the
-//     row's keys live in LDS, three histogram passes of 12 + 12 + 8 bits;
-//   - long rows with few of them (decode): many workgroups per row.  A global
+//   - one workgroup per row when the row has at most 16384 units and there
+//     are at least 128 rows or the row has at most 4096 units: the row's keys
+//     live in LDS, three radix passes of 11 + 11 + 10 bits over a 2048-bin
+//     histogram;
+//   - otherwise (rows longer than 16384 units, or long rows with few of them:
+//     decode): many workgroups per row.  A global
 //     histogram of the top 12 bits (built by the score epilogue in the fused
 //     path) locates the threshold bin; units of that bin are gathered as
 //     candidates; then every chunk's workgroup resolves the exact threshold
@@ -538,7 +541,10 @@ hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
     const void* fn = long_rows ? reinterpret_cast<const void*>(topk_row_kernel<true>)
                                : reinterpret_cast<const void*>(topk_row_kernel<false>);
     if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      // the largest size this path uses (rows of 16384 units), the same value
+      // on every call: no state kept between calls, and concurrent calls agree
+      constexpr size_t lds_max = (ROW_BINS + 16 + 16384 + 16384 / 16 + 1) * sizeof(uint32_t);
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_max));
       if (e != hipSuccess) return e;
     }
     if (long_rows) hipLaunchKernelGGL(topk_row_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);

@@ -4,10 +4,11 @@ The pooled keys persist in a caller buffer across micro-batches; each call
 re-pools only the blocks from a per-sequence first block up to the
 sequence's complete blocks, and a sequence edit re-pools from its position on
 (offgrid-sys llama-memory-hybrid-idx.h: persistent pooled keys, pools to
-re-pool per micro-batch, stale position of an edit).  The bar: the buffer
-after any series of updates equals the one-shot pool of the final keys bit
-for bit, blocks outside every update keep their sentinel, and the one-shot
-pool matches the float64 oracle.
+re-pool per micro-batch, stale position of an edit).  The bar: after every
+call the buffer matches oracle.block_pool_update applied to the same series
+of calls (f32 sums of c rows against float64: rtol 2e-6), which also fixes
+which blocks keep their sentinel; and the buffer after any series of updates
+equals the library's one-shot pool of the final keys bit for bit.
 """
 
 import numpy as np
@@ -29,16 +30,28 @@ def i32(v):
     return torch.tensor(v, dtype=torch.int32, device=DEV)
 
 
+def matches_oracle(pooled, want):
+    got = pooled.cpu().double().numpy()
+    sent = want == SENTINEL
+    assert np.array_equal(got == SENTINEL, sent), "the blocks written differ from the oracle's"
+    assert np.allclose(got[~sent], want[~sent], rtol=2e-6, atol=1e-6)
+
+
 def test_micro_batches_then_edit_equal_one_shot():
     k = inputs.raw_key_batch(3, N_KV, seed=3001).to(DEV)
     nb = N_KV // C
     pooled = torch.full((3, nb, 128), SENTINEL, dtype=torch.float32, device=DEV)
+    want = np.full((3, nb, 128), SENTINEL)
     # three micro-batches with a different stored length per sequence; each
     # call re-pools from the first block the previous call left incomplete
     steps = [[700, 64, 0], [1500, 64, 1000], [N_KV, 2000, N_KV]]
     prev = [0, 0, 0]
+    k64 = O.to_f64(k.cpu())
     for kv in steps:
-        dsa.block_pool_update(k, C, pooled, i32([p // C for p in prev]), kv_len=i32(kv))
+        first = [p // C for p in prev]
+        dsa.block_pool_update(k, C, pooled, i32(first), kv_len=i32(kv))
+        want = O.block_pool_update(k64, C, want, first, kv)
+        matches_oracle(pooled, want)
         prev = kv
     final_blocks = [kv // C for kv in steps[-1]]
     ref = dsa.block_pool(k, C)
@@ -50,18 +63,19 @@ def test_micro_batches_then_edit_equal_one_shot():
     # an edit of sequence 1 from position 1000 stales its pools from block 1000 // 64 on;
     # the other sequences ask for nothing (their first block is past their complete blocks)
     k[1, 1000:] = inputs.raw_key_batch(1, N_KV - 1000, seed=3002).to(DEV)[0]
-    dsa.block_pool_update(k, C, pooled, i32([final_blocks[0], 1000 // C, final_blocks[2]]), kv_len=i32(steps[-1]))
+    first = [final_blocks[0], 1000 // C, final_blocks[2]]
+    dsa.block_pool_update(k, C, pooled, i32(first), kv_len=i32(steps[-1]))
+    want = O.block_pool_update(O.to_f64(k.cpu()), C, want, first, steps[-1])
+    matches_oracle(pooled, want)
     ref2 = dsa.block_pool(k, C)
     torch.cuda.synchronize()
     assert torch.equal(pooled[1, :final_blocks[1]], ref2[1, :final_blocks[1]])
     assert torch.equal(pooled[0], ref2[0]) and torch.equal(pooled[2], ref2[2])
-    # and the one-shot pool against the float64 oracle (f32 sums of 64 bf16 rows)
-    want = O.block_pool(O.to_f64(k.cpu()), C)
-    assert np.allclose(ref2.cpu().double().numpy(), want, rtol=2e-6, atol=1e-6)
 
 
 def test_update_without_lengths_covers_all_complete_blocks():
     k = inputs.raw_key_batch(2, N_KV, dtype=torch.float16, seed=3003).to(DEV)
     pooled = torch.full((2, N_KV // C, 128), SENTINEL, dtype=torch.float32, device=DEV)
     dsa.block_pool_update(k, C, pooled, i32([0, -5]))   # a negative first block counts as 0
+    matches_oracle(pooled, O.block_pool_update(O.to_f64(k.cpu()), C, np.full(tuple(pooled.shape), SENTINEL), [0, -5]))
     assert torch.equal(pooled, dsa.block_pool(k, C))
