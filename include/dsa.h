@@ -42,10 +42,12 @@
  *    innermost.  The caller allocates every buffer, including the workspace
  *    (16-byte aligned, like every tensor pointer, else DSA_ERR_ALIGN);
  *    the library allocates nothing, keeps no pointer after returning and holds
- *    no global state.  Calls are asynchronous on the given stream (a
+ *    no global state (the one exception is dsa_topk_noalloc's static device
+ *    scratch, described there).  Calls are asynchronous on the given stream (a
  *    hipStream_t passed as void*; NULL = the default stream); buffers must stay
  *    alive until the stream reaches them.  Entry points are thread-safe and
- *    re-entrant.
+ *    re-entrant (dsa_topk_noalloc calls that overlap on one GPU race on its
+ *    shared scratch).
  *  - Every argument check runs on the host before anything is launched.  On
  *    failure the call returns a negative DSA_ERR_* code and writes nothing.
  *  - Positions: key j of a sequence is its cache row j, at position j.  A query
@@ -156,6 +158,26 @@ typedef struct {
 size_t dsa_topk_workspace_bytes(const dsa_topk_desc* d);
 int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * S3 without allocation: dsa_topk with the library's own device scratch
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * selection as dsa_topk, with its multi-block workspace (histograms,
+ * candidate counters, candidates) taken from a static device array of
+ * DSA_TOPK_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends.
+ * The call allocates nothing (no hipMalloc, no library allocation).  Calls
+ * whose dsa_topk_workspace_bytes(d) exceeds the array return
+ * DSA_ERR_WORKSPACE and write nothing (16 MiB covers, e.g., 32 rows of 32768
+ * units or 8 rows of 131072).  The stream must belong to the current device.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (the call clears what must start at zero): calls that overlap on
+ * one GPU (other threads, other streams) race and must be serialised by the
+ * caller.
+ * ---------------------------------------------------------------------- */
+#define DSA_TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dsa_topk_noalloc(const float* scores, const dsa_topk_desc* d, int32_t* idx, void* stream);
 
 /* ------------------------------------------------------------------------
  * S1: block pooling                              [QSA]

@@ -17,7 +17,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["index_scores", "topk", "block_pool", "sparse_attn", "forward", "lib", "DsaError",
+__all__ = ["index_scores", "topk", "topk_noalloc", "block_pool", "sparse_attn", "forward", "lib", "DsaError",
            "forward_workspace_bytes", "Event"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,7 @@ SYMBOLS = {
     "dsa_index_scores": (ctypes.c_int, [ctypes.POINTER(IndexDesc), _vp, _vp]),
     "dsa_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(TopkDesc)]),
     "dsa_topk": (ctypes.c_int, [_vp, ctypes.POINTER(TopkDesc), _vp, _vp, ctypes.c_size_t, _vp]),
+    "dsa_topk_noalloc": (ctypes.c_int, [_vp, ctypes.POINTER(TopkDesc), _vp, _vp]),
     "dsa_block_pool": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
     "dsa_block_pool_update": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "dsa_index_share_source": (ctypes.c_int32, [ctypes.c_int32]),
@@ -177,6 +178,19 @@ def topk(scores, q_pos, top_k: int, *, c: int = 1, n_sink: int = 0, kv_len=None,
     nbytes = lib().dsa_topk_workspace_bytes(ctypes.byref(d))
     ws = torch.empty(max(nbytes, 1), device=scores.device, dtype=torch.uint8)
     _check(lib().dsa_topk(_ptr(scores.contiguous()), ctypes.byref(d), _ptr(out), _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def topk_noalloc(scores, q_pos, top_k: int, *, c: int = 1, n_sink: int = 0, kv_len=None, out=None):
+    """dsa_topk on the library's static device scratch (dsa_topk_noalloc):
+    allocates nothing on the device when `out` is given.  Calls that overlap
+    on one GPU race on the shared scratch."""
+    _need_gpu(scores, q_pos, kv_len)
+    S, n_q, n_units = scores.shape
+    if out is None:
+        out = torch.empty((S, n_q, top_k // c), device=scores.device, dtype=torch.int32)
+    d = _topk_desc(S, n_q, n_units, q_pos, kv_len, top_k, c, n_sink)
+    _check(lib().dsa_topk_noalloc(_ptr(scores.contiguous()), ctypes.byref(d), _ptr(out), _stream()))
     return out
 
 

@@ -4,10 +4,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
 
 using namespace dsa;
+
+// The device scratch of dsa_topk_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is a stand-in, not a device address); it passes the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[DSA_TOPK_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -146,6 +154,27 @@ TopkParams topk_params(const float* scores, const dsa_topk_desc* d, int32_t* idx
   return p;
 }
 
+// ------------------------------------------------ the no-allocation top-k --
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Address of the current device's scratch, looked up once per device.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +247,21 @@ int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx, void* wo
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
   TopkParams p = topk_params(scores, d, idx);
   if (need) topk_bind_workspace(p, workspace);
+  return hip_status(launch_topk(p, false, as_stream(stream)));
+}
+
+int dsa_topk_noalloc(const float* scores, const dsa_topk_desc* d, int32_t* idx, void* stream) {
+  const int st = check_topk(scores, d, idx);
+  if (st) return st;
+  const size_t need = dsa_topk_workspace_bytes(d);
+  if (need > DSA_TOPK_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  TopkParams p = topk_params(scores, d, idx);
+  if (need) {
+    void* ws = nullptr;
+    const int sst = scratch_of_current_device(&ws);
+    if (sst) return sst;
+    topk_bind_workspace(p, ws);   // the clear kernel zeroes the histograms and counters first
+  }
   return hip_status(launch_topk(p, false, as_stream(stream)));
 }
 

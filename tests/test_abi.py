@@ -90,6 +90,20 @@ def test_topk_rejects(kw, code):
 
 
 @no_gpu
+@pytest.mark.parametrize("kw,code", [({"top_k": 0}, PARAM), ({"S": 0}, SHAPE), ({"q_pos": None}, NULL),
+                                     ({"S": 16, "n_q": 1, "n_units": 131072, "top_k": 2048}, WORKSPACE)])
+def test_topk_noalloc_rejects(kw, code):
+    # the same argument checks as dsa_topk, and a workspace beyond the 16 MiB
+    # static scratch is refused before the scratch is even looked up
+    L = dsa.lib()
+    d = TopkDesc(FAKE, None, 1, 4, 1000, 64, 1, 0, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    assert L.dsa_topk_noalloc(ctypes.c_void_p(FAKE), ctypes.byref(d), ctypes.c_void_p(FAKE), None) == code
+    assert L.dsa_topk_noalloc(None, ctypes.byref(d), ctypes.c_void_p(FAKE), None) == NULL
+
+
+@no_gpu
 def test_topk_workspace_rule():
     L = dsa.lib()
     short = TopkDesc(FAKE, None, 1, 4096, 4096, 2048, 1, 0, 0)
