@@ -164,13 +164,14 @@ int dsa_topk(const float* scores, const dsa_topk_desc* d, int32_t* idx,
  *
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * selection as dsa_topk, with its multi-block workspace (histograms,
- * candidate counters, candidates) taken from a static device array of
+ * selection as dsa_topk, with its long-row workspace (histograms,
+ * candidate counters, candidates; or the staged units of many long rows)
+ * taken from a static device array of
  * DSA_TOPK_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends.
  * The call allocates nothing (no hipMalloc, no library allocation).  Calls
  * whose dsa_topk_workspace_bytes(d) exceeds the array return
- * DSA_ERR_WORKSPACE and write nothing (16 MiB covers, e.g., 32 rows of 32768
- * units or 8 rows of 131072).  The stream must belong to the current device.
+ * DSA_ERR_WORKSPACE and write nothing (16 MiB covers, e.g., 60 rows of 32768
+ * units or 15 rows of 131072).  The stream must belong to the current device.
  * Every call on a GPU shares that GPU's array, which keeps the last call's
  * contents (the call clears what must start at zero): calls that overlap on
  * one GPU (other threads, other streams) race and must be serialised by the

@@ -260,7 +260,7 @@ int dsa_topk_noalloc(const float* scores, const dsa_topk_desc* d, int32_t* idx, 
     void* ws = nullptr;
     const int sst = scratch_of_current_device(&ws);
     if (sst) return sst;
-    topk_bind_workspace(p, ws);   // the clear kernel zeroes the histograms and counters first
+    topk_bind_workspace(p, ws);   // the kernels clear what must start at zero
   }
   return hip_status(launch_topk(p, false, as_stream(stream)));
 }
@@ -499,7 +499,9 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
       sp.k = pooled;
     }
     TopkParams tp = topk_params(scores, &f.topk_desc, idx);
-    const bool fuse_hist = f.multiblock && scores_use_mfma(sp.q_dtype, sp.k_dtype, sp.H, sp.D);
+    // few long rows: the score epilogue builds the top-k histogram ([FIDX])
+    const bool fuse_hist = f.multiblock && !topk_use_long(rows, f.n_units) &&
+                           scores_use_mfma(sp.q_dtype, sp.k_dtype, sp.H, sp.D);
     if (f.multiblock) {
       topk_bind_workspace(tp, ws + f.off_topk);
       if (fuse_hist) {

@@ -54,7 +54,7 @@ struct TopkParams {
   // multi-block path workspace
   uint32_t* hist;        // [rows][HIST_BINS]
   uint32_t* cand_cnt;    // [rows]
-  uint32_t* cand;        // [rows][cand_cap][2] (key, index)
+  uint32_t* cand;        // [rows][cand_cap][2] (key, index): candidates, or the long-row path's staged units
   uint32_t* cnt_hi;      // [rows][n_chunks]
   uint32_t* thr;         // [rows][4]: b1, -, -, units above b1
   int64_t cand_cap;
@@ -62,7 +62,12 @@ struct TopkParams {
   int32_t n_chunks;
 };
 constexpr int TOPK_CHUNK = 4096;
+// Long rows take the multi-block path: few of them (decode) spread over many
+// workgroups per row (fused or standalone histogram, select, finish); many of
+// them (topk_use_long) one workgroup of 1024 threads per row, whose
+// workspace holds only the staged units.
 bool topk_use_multiblock(int64_t rows, int64_t n_units);
+bool topk_use_long(int64_t rows, int64_t n_units);
 size_t topk_workspace_bytes(int64_t rows, int64_t n_units);
 // Carves the multi-block workspace out of `ws` (256-byte aligned pieces).
 void topk_bind_workspace(TopkParams& p, void* ws);

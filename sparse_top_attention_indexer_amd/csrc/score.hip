@@ -463,10 +463,10 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
 // Decode variant (rows with the fused top-k histogram, 1- or 2-byte keys):
 // one wave per (query row, chunk of 32-key tiles), four chunks of one row per
 // workgroup, one wave per SIMD.  Each wave streams its own key tiles with
-// coalesced loads (every load instruction moves 1 KB of contiguous key rows;
-// a lane-per-key load would touch 64 cache lines per instruction for 16
-// bytes each) through a ring of four tiles in registers (four tiles in flight
-// per wave keep enough bytes moving to cover the loaded memory latency), and
+// coalesced non-temporal loads (every load instruction moves 1 KB of
+// contiguous key rows; a lane-per-key load would touch 64 cache lines per
+// instruction for 16 bytes each) through a ring of four tiles in registers
+// (the loads of three tiles stay in flight while one is stored), and
 // writes each tile into one of two LDS buffers from which the B operands are
 // read in the MFMA layout.  Row r of a tile keeps its 16-byte chunk c in slot
 // c ^ swz(r) (2-byte keys: 256-byte rows, swz(r) = r & 15; fp8: 128-byte
@@ -514,9 +514,9 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
   const int chunk = (static_cast<int>(blockIdx.x) - row32 * ncg) * 4 + wid;
   const int s = row32 / p.n_q;
   const bool active = chunk < p.n_chunks;
-  const int64_t u_begin = static_cast<int64_t>(chunk) * p.chunk_tiles * 32;
-  int64_t u_end = u_begin + static_cast<int64_t>(p.chunk_tiles) * 32;
-  if (u_end > p.n_units) u_end = p.n_units;
+  const int tiles_row = static_cast<int>((p.n_units + 31) >> 5);
+  // local tile j of this wave is tile chunk + j * n_chunks of the row
+  auto tile_of = [&](int j) -> int64_t { return static_cast<int64_t>(chunk) + static_cast<int64_t>(j) * p.n_chunks; };
 
   // load i of a tile covers the 1 KB of rows 1024 i / ROW ..; lane L takes
   // the 16 bytes that belong at byte 16 L of it: row r = (1024 i + 16 L) / ROW,
@@ -534,25 +534,35 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
       loff[i] = static_cast<uint32_t>(r) * 128u + 16u * ((lane & 7) ^ ((r >> 1) & 7));
     }
   }
+  // Every load is unconditional, at an in-range address: rows past the cache
+  // reload the tile's last stored row (their scores are never written), and
+  // the caller clamps the tile index.  With no predicate on any load, the
+  // compiler counts the ring's loads exactly (a wait for the oldest tile
+  // only) instead of draining all of them before each LDS store.  The keys
+  // are streamed once, so the loads are non-temporal.
   auto load_tile = [&](StreamTile<KK>& tt, int j) __attribute__((always_inline)) {
-    const int64_t ut = u_begin + static_cast<int64_t>(j) * 32;
+    const int64_t ut = tile_of(j) * 32;
     const char* tb = kbase + ut * G::ROW;
-    const int64_t lim = (p.n_units - ut) * G::ROW;   // bytes of the tile inside the cache
+    const int64_t lim = (p.n_units - ut) * G::ROW;   // bytes of the tile inside the cache (>= one row)
 #pragma unroll
-    for (int i = 0; i < G::NLD; ++i)
-      tt.v[i] = static_cast<int64_t>(loff[i]) < lim ? *reinterpret_cast<const u32x4_t*>(tb + loff[i])
-                                                    : u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (KK == KK_FP8) tt.sc = ut + n < p.n_units ? sbase[ut + n] : 0.f;
+    for (int i = 0; i < G::NLD; ++i) {
+      const uint32_t o = static_cast<int64_t>(loff[i]) < lim
+                             ? loff[i]
+                             : static_cast<uint32_t>(lim - G::ROW) + (loff[i] & (G::ROW - 1));
+      tt.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(tb + o));
+    }
+    if constexpr (KK == KK_FP8) tt.sc = sbase[ut + n < p.n_units ? ut + n : p.n_units - 1];
   };
   // The first NR tiles of the chunk are requested before anything else (the
   // visible length is not known yet: tiles past it are loaded, never used),
   // so that the keys stream while q is loaded and converted.
   constexpr int NR = stream_occupancy<KK>() == 2 ? 2 : 4;
   StreamTile<KK> rr[NR];
-  const int n_pre = active ? static_cast<int>((u_end - u_begin + 31) >> 5) : 0;   // tiles of the chunk
+  const int n_pre = active && chunk < tiles_row ? (tiles_row - chunk + p.n_chunks - 1) / p.n_chunks : 0;
+  if (n_pre > 0) {
 #pragma unroll
-  for (int k = 0; k < NR; ++k)
-    if (k < n_pre) load_tile(rr[k], k);
+    for (int k = 0; k < NR; ++k) load_tile(rr[k], k < n_pre ? k : n_pre - 1);
+  }
 
   const int32_t qpos = p.q_pos[row];
   const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
@@ -562,10 +572,10 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
   for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = 0;
 
   const int64_t n_vis = visible_tokens(qpos, kl, p.n_units * p.c) / p.c;
-  const int64_t c_end = n_vis < u_end ? n_vis : u_end;   // compute [u_begin, c_end)
   const bool do_hist = n_vis > p.k_out;
   const int64_t nf = (p.c == 1 && p.n_sink < n_vis) ? p.n_sink : (p.c == 1 ? n_vis : 0);
-  const int n_t = active && c_end > u_begin ? static_cast<int>((c_end - u_begin + 31) >> 5) : 0;
+  const int t_vis = static_cast<int>((n_vis + 31) >> 5);   // tiles with a visible unit
+  const int n_t = active && chunk < t_vis ? (t_vis - chunk + p.n_chunks - 1) / p.n_chunks : 0;
 
   const uint32_t wbase = static_cast<uint32_t>(wid) * (2 * G::TB);
   auto store_tile = [&](const StreamTile<KK>& tt, int buf) __attribute__((always_inline)) {
@@ -621,7 +631,7 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
       for (int jj = 0; jj < 16; ++jj) part[jj & 3] = fmaf(wv[rb][jj], relu(acc[rb][jj]), part[jj & 3]);
     float tot = half_sum((part[0] + part[1]) + (part[2] + part[3]));
     if constexpr (KK == KK_FP8) tot *= sc;
-    const int64_t u = u_begin + static_cast<int64_t>(j) * 32 + n;
+    const int64_t u = tile_of(j) * 32 + n;
     const float val = u < n_vis ? tot : NEG_INF;
     if (h2 == 0) {
       so[j * 32 + n] = val;
@@ -629,45 +639,46 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
     }
   };
 
-  // tile j + k sits in LDS buffer k & 1 (j a multiple of NR, NR even); the
-  // NR tiles after the next one are in flight in the register ring
+  // Tile t sits in ring slot t % NR until it is written into LDS buffer
+  // t & 1; step j writes tile j + 1 (loaded NR - 1 steps earlier), refills
+  // its slot with tile j + 1 + NR (clamped to the last tile), then computes
+  // tile j.  The steps run in whole rounds of NR: past the last tile a step
+  // only stores and reloads (the compute is skipped by a uniform branch), so
+  // every round issues the same loads and the wait before a store is always
+  // for the oldest tile in flight alone.
   float scb[2] = {0.f, 0.f};   // fp8 scales of the tiles in the LDS buffers
   __syncthreads();   // the histogram is clear
   if (n_t > 0) {
+    const int last = n_t - 1;
     store_tile(rr[0], 0);
     scb[0] = rr[0].sc;
-    if (NR < n_t) load_tile(rr[0], NR);
-  }
-  auto step = [&](auto kc, int j) __attribute__((always_inline)) {
-    constexpr int k = decltype(kc)::value;
-    constexpr int k1 = (k + 1) % NR;
-    const int jj = j + k;
-    if (jj >= n_t) return;
-    if (jj + 1 < n_t) {
-      store_tile(rr[k1], (k + 1) & 1);   // over tile jj - 1, read by the previous step
+    load_tile(rr[0], NR < last ? NR : last);
+    auto step = [&](auto kc, int j) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int k1 = (k + 1) % NR;
+      store_tile(rr[k1], (k + 1) & 1);   // tile j + 1, over tile j - 1 (read by the previous step)
       scb[(k + 1) & 1] = rr[k1].sc;
-    }
-    if (jj + 1 + NR < n_t) load_tile(rr[k1], jj + 1 + NR);
-    compute(jj, scb[k & 1]);
-  };
-  for (int j = 0; j < n_t; j += NR) {
-    step(std::integral_constant<int, 0>{}, j);
-    step(std::integral_constant<int, 1>{}, j);
-    if constexpr (NR == 4) {
-      step(std::integral_constant<int, 2>{}, j);
-      step(std::integral_constant<int, 3>{}, j);
+      const int jn = j + 1 + NR;
+      load_tile(rr[k1], jn < last ? jn : last);
+      if (j < n_t) compute(j, scb[k & 1]);
+    };
+    for (int j = 0; j < n_t; j += NR) {
+      step(std::integral_constant<int, 0>{}, j);
+      step(std::integral_constant<int, 1>{}, j + 1);
+      if constexpr (NR == 4) {
+        step(std::integral_constant<int, 2>{}, j + 2);
+        step(std::integral_constant<int, 3>{}, j + 3);
+      }
     }
   }
-  // write-out of the wave's chunk: computed tiles, then -inf for the
+  // write-out of the wave's tiles: computed ones, then -inf for the
   // invisible rest when asked
   if (active) {
-    const int64_t done = u_begin + static_cast<int64_t>(n_t) * 32 < u_end ? u_begin + static_cast<int64_t>(n_t) * 32
-                                                                         : u_end;
-    const int64_t w_end = p.fill_invisible ? u_end : done;
     float* orow = p.scores + row * p.n_units;
-    for (int64_t u = u_begin + lane; u < w_end; u += 64) {
-      const int i = static_cast<int>(u - u_begin);
-      orow[u] = i < n_t * 32 ? so[i] : NEG_INF;
+    for (int i = lane; i < n_pre * 32; i += 64) {
+      const int j = i >> 5;
+      const int64_t u = tile_of(j) * 32 + (i & 31);
+      if (u < p.n_units && (j < n_t || p.fill_invisible)) orow[u] = j < n_t ? so[i] : NEG_INF;
     }
   }
   __syncthreads();

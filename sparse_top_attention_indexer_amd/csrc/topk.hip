@@ -16,10 +16,15 @@
 //     are at least 128 rows or the row has at most 4096 units: the row's keys
 //     live in LDS, three radix passes of 11 + 11 + 10 bits over a 2048-bin
 //     histogram;
-//   - otherwise (rows longer than 16384 units, or long rows with few of them:
-//     decode): many workgroups per row.  A global
-//     histogram of the top 12 bits (built by the score epilogue in the fused
-//     path) locates the threshold bin; units of that bin are gathered as
+//   - many long rows (at least 128 rows of more than 16384 units): one
+//     workgroup of 1024 threads per row, whose two passes over the row's
+//     scores (the second from L2) find the threshold bin and stage the units
+//     at or above it in index order; the exact threshold comes from the
+//     staged units of that bin, and a last compaction of the short staged
+//     list writes the kept ids (topk_long_kernel);
+//   - few long rows (decode): many workgroups per row.  A global histogram
+//     of the top 12 bits (built by the score epilogue in the fused path)
+//     locates the threshold bin; units of that bin are gathered as
 //     candidates; then every chunk's workgroup resolves the exact threshold
 //     among the row's candidates itself and compacts its chunk.
 #include "dsa_device.h"
@@ -492,16 +497,332 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkParams p) {
   }
 }
 
+// ------------------------------------------------------------- long rows --
+
+constexpr int LONG_NT = 1024;                 // threads of the long-row kernel (16 waves)
+constexpr int LONG_NW = LONG_NT / 64;
+constexpr int LONG_SUB = 4 * LONG_NT;         // units of one coalesced sub-block (a float4 per thread)
+constexpr int LONG_NS = 4;                    // sub-blocks per iteration
+constexpr int LONG_IT = LONG_NS * LONG_SUB;   // 16384 units per iteration
+constexpr int LONG_BINS = 4096;               // 12-bit histogram
+constexpr int LONG_COPIES = 8;                // histogram copies (lane l adds into copy l % 8)
+constexpr int LONG_STRIDE = LONG_BINS + 1;    // words between copies: a bin's copies fall in different banks
+constexpr size_t LONG_LDS = static_cast<size_t>(LONG_COPIES) * LONG_STRIDE * sizeof(uint32_t);
+
+// Finds the bin b (scanning from the highest bin down) that holds the need-th
+// largest element: above(b) < need <= above(b) + hist[b].  NT threads, nb a
+// multiple of NT (at most 16 bins per thread).  All threads get the result.
+template <int NT>
+__device__ uint32_t find_bin_desc_nt(const uint32_t* hist, int nb, uint32_t need, uint32_t* scratch,
+                                     uint32_t* above) {
+  const int per = nb / NT;
+  const int hi = nb - threadIdx.x * per;
+  uint32_t c[16];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c[i] = i < per ? hist[hi - 1 - i] : 0u;
+    local += c[i];
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<NT / 64>(local, scratch, &total);
+  if (excl < need && need <= excl + local) {
+    uint32_t acc = excl, acc_at = 0;
+    int found = per - 1;
+    bool done = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (!done && i < per) {
+        if (acc + c[i] >= need) {
+          found = i;
+          acc_at = acc;
+          done = true;
+        }
+        acc += c[i];
+      }
+    }
+    scratch[NT / 64] = static_cast<uint32_t>(hi - 1 - found);
+    scratch[NT / 64 + 1] = acc_at;
+  }
+  __syncthreads();
+  const uint32_t bin = scratch[NT / 64];
+  *above = scratch[NT / 64 + 1];
+  __syncthreads();
+  return bin;
+}
+
+// Raw scores of one iteration of the long-row kernel: thread t holds units
+// a + 4096 i + 4 t + r (sub-block i < 4, r < 4), so that every load
+// instruction of a wave reads 1 KB of contiguous scores.  Every load is
+// unconditional at an in-range address, so that the next iteration's loads
+// stay in flight while this one is processed: ALIGNED (units a multiple of
+// 4, rows 16-byte aligned) loads float4s, clamped to the last whole one
+// (whose units, past the row, are never used); otherwise one clamped load
+// per unit.
+template <bool ALIGNED>
+__device__ __forceinline__ void long_load(const float* sc, int64_t n_units, int64_t a, float (&v)[4 * LONG_NS]) {
+#pragma unroll
+  for (int i = 0; i < LONG_NS; ++i) {
+    const int64_t u0 = a + static_cast<int64_t>(i) * LONG_SUB + 4 * threadIdx.x;
+    if constexpr (ALIGNED) {
+      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(sc + (u0 + 4 <= n_units ? u0 : n_units - 4));
+      v[4 * i] = q[0];
+      v[4 * i + 1] = q[1];
+      v[4 * i + 2] = q[2];
+      v[4 * i + 3] = q[3];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * i + r] = sc[u0 + r < n_units ? u0 + r : n_units - 1];
+    }
+  }
+}
+
+// Keys of the loaded units; bit 4 i + r of the result says the unit lies in [lo, hi).
+__device__ __forceinline__ uint32_t long_keys(const float (&v)[4 * LONG_NS], int64_t a, int64_t lo, int64_t hi,
+                                              uint32_t (&key)[4 * LONG_NS]) {
+  uint32_t valid = 0;
+#pragma unroll
+  for (int i = 0; i < LONG_NS; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t u = a + static_cast<int64_t>(i) * LONG_SUB + 4 * threadIdx.x + r;
+      key[4 * i + r] = order_key(v[4 * i + r]);
+      valid |= static_cast<uint32_t>(u >= lo && u < hi) << (4 * i + r);
+    }
+  return valid;
+}
+
+// Ordered compaction of one iteration: writes the selected units (bit 4 i + r
+// of sel: unit a + 4096 i + 4 t + r) at base + their rank in index order
+// (sub-blocks, then waves, then lanes, then r), through put(position, slot);
+// returns the number selected.  A lane's selected units of lower lanes come
+// from the four ballots of its sub-block; per-wave totals through LDS.  All
+// threads call it; it holds two barriers.
+template <typename F>
+__device__ __forceinline__ uint32_t long_compact(uint32_t sel, uint32_t base, uint32_t* s_wt, F&& put) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t lane_before[LONG_NS];
+#pragma unroll
+  for (int i = 0; i < LONG_NS; ++i) {
+    uint32_t lb = 0, wt = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t bal = __ballot((sel >> (4 * i + r)) & 1u);
+      lb += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+      wt += static_cast<uint32_t>(__popcll(bal));
+    }
+    lane_before[i] = lb;
+    if (lane == 0) s_wt[i * LONG_NW + wid] = wt;
+  }
+  __syncthreads();
+  uint32_t sub_base = 0;
+#pragma unroll
+  for (int i = 0; i < LONG_NS; ++i) {
+    uint32_t before = 0, st = 0;
+    for (int w = 0; w < LONG_NW; ++w) {
+      const uint32_t t = s_wt[i * LONG_NW + w];
+      before += w < wid ? t : 0u;
+      st += t;
+    }
+    uint32_t pos = base + sub_base + before + lane_before[i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if ((sel >> (4 * i + r)) & 1u) {
+        put(pos, 4 * i + r);
+        ++pos;
+      }
+    }
+    sub_base += st;
+  }
+  __syncthreads();   // s_wt is rewritten by the next call
+  return sub_base;
+}
+
+// One workgroup of 1024 threads per row, for rows longer than the row kernel
+// holds in LDS, and for the few long rows of decode.  The row's scores are
+// read twice (the second time from the L2), each pass with the next
+// iteration's loads in flight while the current one is processed:
+//   1. a histogram of the top 12 bits of the keys of the candidate units (the
+//      visible units past the forced sinks), in eight bank-shifted copies
+//      (lane l adds into copy l % 8, so that lanes of one instruction rarely
+//      hit one address), finds the threshold bin b1;
+//   2. every unit at or above bin b1 is staged in the workspace as (key,
+//      index), in index order (ordered compaction: ballots within a wave,
+//      per-wave totals through LDS): the kept units of bins above b1 plus
+//      the units of bin b1, a few thousand for a real score row;
+// then the staged units of bin b1 give the exact threshold key T and, when
+// the tie at T is cut, the largest kept index J among the units equal to T;
+// a last ordered compaction over the staged list writes the kept ids in
+// ascending order.  The staging count lives in registers (one workgroup per
+// row), so nothing needs clearing before the launch.
+template <bool ALIGNED>
+__device__ void topk_long_row(const TopkParams& p, int64_t row, uint32_t* s_hist, uint32_t* s_scr, uint32_t* s_wt) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const RowInfo ri = row_info(p, row);
+  int32_t* out = p.idx + row * p.k_out;
+  if (ri.n_vis <= p.k_out) {   // everything visible is kept
+    for (int64_t j = tid; j < p.k_out; j += LONG_NT) out[j] = j < ri.n_vis ? static_cast<int32_t>(j) : -1;
+    return;
+  }
+  for (int64_t j = tid; j < p.k_out; j += LONG_NT) {
+    if (j < ri.nf) out[j] = static_cast<int32_t>(j);
+    else if (j >= ri.K) out[j] = -1;
+  }
+  uint32_t need = static_cast<uint32_t>(ri.K - ri.nf);
+  if (need == 0) return;   // every kept slot is a forced sink
+  const float* sc = p.scores + row * p.n_units;
+  const int64_t lo = ri.nf, hi = ri.n_vis;
+  const int64_t a_end = (hi + LONG_IT - 1) / LONG_IT * LONG_IT;   // whole iterations covering [0, hi)
+
+  // pass 1: histogram of the top 12 bits
+  for (int b = tid; b < LONG_COPIES * LONG_STRIDE; b += LONG_NT) s_hist[b] = 0;
+  __syncthreads();
+  uint32_t* my_hist = s_hist + (lane & (LONG_COPIES - 1)) * LONG_STRIDE;
+  {
+    float cur[4 * LONG_NS];
+    long_load<ALIGNED>(sc, p.n_units, 0, cur);
+    for (int64_t a = 0; a < a_end; a += LONG_IT) {
+      float nxt[4 * LONG_NS];
+      long_load<ALIGNED>(sc, p.n_units, a + LONG_IT < a_end ? a + LONG_IT : a, nxt);
+      uint32_t k[4 * LONG_NS];
+      const uint32_t v = long_keys(cur, a, lo, hi, k);
+#pragma unroll
+      for (int i = 0; i < 4 * LONG_NS; ++i)
+        if ((v >> i) & 1u) atomicAdd(&my_hist[k[i] >> 20], 1u);
+#pragma unroll
+      for (int i = 0; i < 4 * LONG_NS; ++i) cur[i] = nxt[i];
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < LONG_BINS; b += LONG_NT) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < LONG_COPIES; ++c) t += s_hist[c * LONG_STRIDE + b];
+    s_hist[b] = t;   // copy 0 holds the sum (each bin has one owner thread)
+  }
+  __syncthreads();
+  uint32_t above;
+  const uint32_t b1 = find_bin_desc_nt<LONG_NT>(s_hist, LONG_BINS, need, s_scr, &above);
+  need -= above;   // to keep from bin b1
+
+  // pass 2: stage the units at or above bin b1, in index order
+  uint32_t* stage = p.cand + row * p.cand_cap * 2;
+  uint32_t m = 0;   // staged units
+  {
+    float cur[4 * LONG_NS];
+    long_load<ALIGNED>(sc, p.n_units, 0, cur);
+    for (int64_t a = 0; a < a_end; a += LONG_IT) {
+      float nxt[4 * LONG_NS];
+      long_load<ALIGNED>(sc, p.n_units, a + LONG_IT < a_end ? a + LONG_IT : a, nxt);
+      uint32_t k[4 * LONG_NS];
+      const uint32_t v = long_keys(cur, a, lo, hi, k);
+      uint32_t sel = 0;
+#pragma unroll
+      for (int i = 0; i < 4 * LONG_NS; ++i) sel |= static_cast<uint32_t>(((v >> i) & 1u) && (k[i] >> 20) >= b1) << i;
+      m += long_compact(sel, m, s_wt, [&](uint32_t pos, int slot) {
+        if (pos < p.cand_cap) {
+          stage[2 * pos] = k[slot];
+          stage[2 * pos + 1] = static_cast<uint32_t>(a + (slot >> 2) * LONG_SUB + 4 * tid + (slot & 3));
+        }
+      });
+#pragma unroll
+      for (int i = 0; i < 4 * LONG_NS; ++i) cur[i] = nxt[i];
+    }
+  }
+  // (long_compact's last barrier: the staged list is complete and visible)
+
+  // exact threshold among the staged units of bin b1: 12 + 8 more bits of the
+  // key, then, only when the tie at T is cut, 11 + 11 + 10 bits of the
+  // complemented index
+  uint32_t prefix = b1 << 20, pmask = 0xfff00000u, n_eq = 0;
+  {
+    const int shifts[2] = {8, 0};
+    const int nbits[2] = {12, 8};
+    for (int pass = 0; pass < 2; ++pass) {
+      const int nb = 1 << nbits[pass], sh = shifts[pass];
+      for (int b = tid; b < LONG_BINS; b += LONG_NT) s_hist[b] = 0;
+      __syncthreads();
+      for (uint32_t e = tid; e < m; e += LONG_NT) {
+        const uint32_t kk = stage[2 * e];
+        if ((kk & pmask) == prefix) atomicAdd(&s_hist[(kk >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t ab;
+      const uint32_t b = find_bin_desc_nt<LONG_NT>(s_hist, LONG_BINS, need, s_scr, &ab);
+      need -= ab;
+      prefix |= b << sh;
+      pmask |= static_cast<uint32_t>(nb - 1) << sh;
+      if (pass == 1) n_eq = s_hist[b];
+      __syncthreads();   // every thread has read s_hist[b] before the next clear
+    }
+  }
+  const uint32_t T = prefix;
+  uint32_t J = 0xffffffffu;   // the largest kept index among the units equal to T
+  if (n_eq > need) {
+    uint32_t jp = 0, jm = 0;
+    const int jsh[3] = {21, 10, 0};
+    const int jbits[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int nb = 1 << jbits[pass], sh = jsh[pass];
+      for (int b = tid; b < LONG_BINS; b += LONG_NT) s_hist[b] = 0;
+      __syncthreads();
+      for (uint32_t e = tid; e < m; e += LONG_NT) {
+        const uint32_t kk = stage[2 * e], cj = ~stage[2 * e + 1];
+        if (kk == T && (cj & jm) == jp) atomicAdd(&s_hist[(cj >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t ab;
+      const uint32_t b = find_bin_desc_nt<LONG_NT>(s_hist, LONG_BINS, need, s_scr, &ab);
+      need -= ab;
+      jp |= b << sh;
+      jm |= static_cast<uint32_t>(nb - 1) << sh;
+    }
+    J = ~jp;
+  }
+
+  // the kept units of the staged list, in its (index) order: thread t owns a
+  // contiguous run of it
+  const uint32_t per = (m + LONG_NT - 1) / LONG_NT;
+  const uint32_t e0 = tid * per < m ? tid * per : m;
+  const uint32_t e1 = e0 + per < m ? e0 + per : m;
+  uint32_t n_keep = 0;
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t kk = stage[2 * e], j = stage[2 * e + 1];
+    n_keep += kk > T || (kk == T && j <= J);
+  }
+  uint32_t tot;
+  uint32_t pos = static_cast<uint32_t>(ri.nf) + block_excl_scan<LONG_NW>(n_keep, s_scr, &tot);
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t kk = stage[2 * e], j = stage[2 * e + 1];
+    if (kk > T || (kk == T && j <= J)) {
+      if (pos < ri.K) out[pos] = static_cast<int32_t>(j);   // guard: never past K
+      ++pos;
+    }
+  }
+}
+
+__global__ __launch_bounds__(LONG_NT) void topk_long_kernel(TopkParams p) {
+  extern __shared__ uint32_t s_hist[];   // LONG_COPIES x LONG_STRIDE
+  __shared__ uint32_t s_scr[LONG_NW + 4];
+  __shared__ uint32_t s_wt[LONG_NS * LONG_NW];   // selected units per (sub-block, wave)
+  if ((p.n_units & 3) == 0) topk_long_row<true>(p, blockIdx.x, s_hist, s_scr, s_wt);
+  else topk_long_row<false>(p, blockIdx.x, s_hist, s_scr, s_wt);
+}
+
 // ------------------------------------------------------------------ host --
 
 bool topk_use_multiblock(int64_t rows, int64_t n_units) {
   return n_units > 16384 || (rows < 128 && n_units > TOPK_CHUNK);
 }
 
+bool topk_use_long(int64_t rows, int64_t n_units) { return rows >= 128 && n_units > 16384; }
+
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n_units) {
   if (!topk_use_multiblock(rows, n_units)) return 0;
+  if (topk_use_long(rows, n_units)) return align256(static_cast<size_t>(rows) * n_units * 8);   // staged units
   const int64_t nch = (n_units + TOPK_CHUNK - 1) / TOPK_CHUNK;
   size_t b = 0;
   b += align256(rows * HIST_BINS * 4);
@@ -514,9 +835,13 @@ size_t topk_workspace_bytes(int64_t rows, int64_t n_units) {
 
 void topk_bind_workspace(TopkParams& p, void* ws) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  p.cand_cap = p.n_units;
+  if (topk_use_long(rows, p.n_units)) {
+    p.cand = static_cast<uint32_t*>(ws);
+    return;
+  }
   p.chunk = TOPK_CHUNK;
   p.n_chunks = static_cast<int32_t>((p.n_units + TOPK_CHUNK - 1) / TOPK_CHUNK);
-  p.cand_cap = p.n_units;
   char* c = static_cast<char*>(ws);
   p.hist = reinterpret_cast<uint32_t*>(c);     c += align256(rows * HIST_BINS * 4);
   p.cand_cnt = reinterpret_cast<uint32_t*>(c); c += align256(rows * 4);
@@ -535,6 +860,7 @@ hipError_t launch_topk_clear(const TopkParams& p, hipStream_t st) {
 
 hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  hipError_t e;
   if (!topk_use_multiblock(rows, p.n_units)) {
     const size_t lds = (ROW_BINS + 16 + static_cast<size_t>(p.n_units + p.n_units / 16 + 1)) * sizeof(uint32_t);
     const bool long_rows = p.n_units > 2048;
@@ -544,15 +870,22 @@ hipError_t launch_topk(const TopkParams& p, bool hist_ready, hipStream_t st) {
       // the largest size this path uses (rows of 16384 units), the same value
       // on every call: no state kept between calls, and concurrent calls agree
       constexpr size_t lds_max = (ROW_BINS + 16 + 16384 + 16384 / 16 + 1) * sizeof(uint32_t);
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_max));
-      if (e != hipSuccess) return e;
+      if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_max))) !=
+          hipSuccess)
+        return e;
     }
     if (long_rows) hipLaunchKernelGGL(topk_row_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
     else hipLaunchKernelGGL(topk_row_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(256), lds, st, p);
     return hipGetLastError();
   }
+  if (topk_use_long(rows, p.n_units)) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_long_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(LONG_LDS))) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(topk_long_kernel, dim3(static_cast<unsigned>(rows)), dim3(LONG_NT), LONG_LDS, st, p);
+    return hipGetLastError();
+  }
   const dim3 g(static_cast<unsigned>(rows * p.n_chunks));
-  hipError_t e;
   if (!hist_ready) {
     if ((e = launch_topk_clear(p, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(topk_hist_kernel, g, dim3(256), 0, st, p);

@@ -91,7 +91,7 @@ def test_topk_rejects(kw, code):
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [({"top_k": 0}, PARAM), ({"S": 0}, SHAPE), ({"q_pos": None}, NULL),
-                                     ({"S": 16, "n_q": 1, "n_units": 131072, "top_k": 2048}, WORKSPACE)])
+                                     ({"S": 17, "n_q": 1, "n_units": 131072, "top_k": 2048}, WORKSPACE)])
 def test_topk_noalloc_rejects(kw, code):
     # the same argument checks as dsa_topk, and a workspace beyond the 16 MiB
     # static scratch is refused before the scratch is even looked up

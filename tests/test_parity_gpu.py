@@ -240,6 +240,23 @@ def test_topk_rows_in_registers_long_rows():
 def test_topk_multiblock_decode_rows():
     _topk_case(3, 1, 40000, 2048, n_sink=1, kv_len=[40000, 25000, 1000], seed=3)
     _topk_case(2, 1, 131072, 2048, seed=4)
+    # a row length that is not a multiple of 4 (unaligned rows: per-unit loads), sinks
+    _topk_case(2, 1, 40001, 2048, n_sink=2, kv_len=[40001, 39999], seed=19)
+
+
+def test_topk_long_rows_thousand_rows():
+    # 1000 rows of 16401 units (row starts not 16-byte aligned: per-unit
+    # loads), ties: the long-row kernel, one workgroup per row
+    _topk_case(1, 1000, 16401, 300, kind="ties", seed=21)
+
+
+def test_topk_long_rows_many_rows():
+    # more than 128 rows of more than 16384 units: one workgroup per row on the
+    # long-row kernel (rows 16-byte aligned: float4 loads), causal lengths from
+    # below top_k to the whole row, ties
+    n = 20000
+    q_pos = torch.arange(0, 130 * 150, 150, dtype=torch.int32)[None]
+    _topk_case(1, 130, n, 1000, q_pos=q_pos, kind="ties", seed=20)
 
 
 def test_topk_multiblock_ties_and_equal():

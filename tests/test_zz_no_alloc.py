@@ -41,14 +41,14 @@ def test_noalloc_topk_equals_topk_on_two_calls_then_refuses_oversize():
         q_pos = torch.full((S, 1), n - 1, dtype=torch.int32, device=DEV)
         kv = torch.tensor([n - 37 * s for s in range(S)], dtype=torch.int32, device=DEV)
         d = dsa._topk_desc(S, 1, n, q_pos, kv, k, 1, sink)
-        assert 0 < dsa.lib().dsa_topk_workspace_bytes(ctypes.byref(d)) <= (16 << 20)
+        assert 0 < dsa.lib().dsa_topk_workspace_bytes(ctypes.byref(d)) <= (16 << 20)   # uses the scratch
         out = torch.full((S, 1, k), -7, dtype=torch.int32, device=DEV)
         assert noalloc(sc, d, out) == 0
         ref = dsa.topk(sc, q_pos, k, n_sink=sink, kv_len=kv)
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
-    # 16 rows of 131072 units need more than the 16 MiB scratch: refused, untouched
-    S, n, k = 16, 131072, 2048
+    # 17 rows of 131072 units need more than the 16 MiB scratch: refused, untouched
+    S, n, k = 17, 131072, 2048
     sc = decode_scores(S, n, 3)
     q_pos = torch.full((S, 1), n - 1, dtype=torch.int32, device=DEV)
     d = dsa._topk_desc(S, 1, n, q_pos, None, k, 1, 0)
