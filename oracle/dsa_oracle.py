@@ -633,6 +633,62 @@ def key_write_check(k_new: np.ndarray, cache_dtype: str, hadamard_k: bool, got, 
 
 
 # --------------------------------------------------------------------------
+# q8_0 latent cache: the quantised form of the gathered rows.
+# --------------------------------------------------------------------------
+#
+# ik_llama_opt log, openPangu port, "Add OpenPangu q8_0 latent cache type":
+# the 576-wide MLA latent rows are cached as q8_0 (0.53x the bytes of f16)
+# and attention reads them back; top-k is bit-identical and attention agrees
+# with the f16 cache to a relative L-inf of 0.0057.  q8_0 is ggml's block
+# format: blocks of 32 consecutive values, each an int8 code times one f16
+# scale per block.  The page fixes the format, not the rounding of the
+# encoder; the reading taken here: scale = f16(max |x| / 127) over the block,
+# code = x / scale rounded to nearest (ties away from zero, as C's roundf),
+# clamped to [-127, 127].  Only decode_q8_0 is on the attention path; the
+# encoder makes test caches and states the round-trip bound.
+
+Q8_BLOCK = 32
+
+
+def decode_q8_0(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """q8_0 rows -> float64, exactly.
+
+    codes int8 [..., n] (n a multiple of 32), scales f16 bit patterns or f16
+    values [..., n / 32]: value(d) = codes(d) * scales(d // 32).
+    """
+    c = np.asarray(codes).astype(np.int64).astype(np.float64)
+    sc = np.asarray(scales)
+    if sc.dtype == np.uint16:
+        sc = decode_f16(sc)
+    sc = np.asarray(sc, dtype=np.float64)
+    if c.shape[-1] != sc.shape[-1] * Q8_BLOCK:
+        raise ValueError("codes and scales disagree on the number of blocks")
+    return c * np.repeat(sc, Q8_BLOCK, axis=-1)
+
+
+def encode_q8_0(x: np.ndarray):
+    """Values [..., n] (n a multiple of 32) -> (codes int8 [..., n], scales f16 [..., n / 32]).
+
+    scale = f16(max |x| / 127) per block; code = round(x / scale) (half away
+    from zero), clamped to [-127, 127]; a zero block stores scale 0 and zero
+    codes.  |decode - x| <= scale / 2 per element, plus the clamp when the
+    f16 rounding made the scale smaller than max |x| / 127.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if n % Q8_BLOCK:
+        raise ValueError("q8_0 rows are whole blocks of 32")
+    blk = x.reshape(x.shape[:-1] + (n // Q8_BLOCK, Q8_BLOCK))
+    amax = np.abs(blk).max(axis=-1)
+    scale = (amax / 127.0).astype(np.float16)
+    s64 = scale.astype(np.float64)
+    q = np.zeros_like(blk)
+    np.divide(blk, s64[..., None], out=q, where=s64[..., None] > 0)
+    code = np.clip(np.sign(q) * np.floor(np.abs(q) + 0.5), -127, 127).astype(np.int8)
+    return code.reshape(x.shape), scale
+
+
+# --------------------------------------------------------------------------
 # IndexShare: layers that reuse an earlier layer's selection.
 # --------------------------------------------------------------------------
 #

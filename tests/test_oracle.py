@@ -592,6 +592,47 @@ def test_block_pool_update_equals_one_shot_after_micro_batches_and_an_edit():
     assert np.all(O.block_pool_update(kc, 8, np.zeros((1, 2, 4)), [-3]) == 2.5)
 
 
+# ------------------------------------------------------------- q8_0 latent --
+
+def test_q8_0_decode_hand_worked_block():
+    # one block with scale 0.5 (f16 0x3800) and codes -127, -1, 0, 1, 2, 127,
+    # then 26 zeros; a second block with scale 2^-10 (f16 0x1400): codes x 2^-10
+    codes = np.zeros(64, dtype=np.int8)
+    codes[:6] = [-127, -1, 0, 1, 2, 127]
+    codes[32:35] = [3, -64, 100]
+    scales = np.array([0x3800, 0x1400], dtype=np.uint16)
+    v = O.decode_q8_0(codes, scales)
+    assert v[:6].tolist() == [-63.5, -0.5, 0.0, 0.5, 1.0, 63.5] and not v[6:32].any()
+    assert v[32:35].tolist() == [3 / 1024, -64 / 1024, 100 / 1024] and not v[35:].any()
+    # the same through f16 values instead of bit patterns
+    assert np.array_equal(O.decode_q8_0(codes, scales.view(np.float16)), v)
+
+
+def test_q8_0_encode_round_trip_bound_and_extremes():
+    g = np.random.default_rng(41)
+    x = g.standard_normal((50, 576))
+    x[3] *= 8.0                          # an outlier row
+    x[5, :32] = 0.0                      # a zero block
+    x[7, 64:96] = np.linspace(-3, 3, 32)
+    codes, scales = O.encode_q8_0(x)
+    assert codes.dtype == np.int8 and scales.dtype == np.float16 and scales.shape == (50, 18)
+    assert scales[5, 0] == 0 and not codes[5, :32].any()
+    dec = O.decode_q8_0(codes, scales)
+    s = np.repeat(scales.astype(np.float64), 32, axis=-1)
+    amax = np.repeat(np.abs(x.reshape(50, 18, 32)).max(-1), 32, axis=-1)
+    # half a step, plus what the clamp at 127 can cut when the f16 scale
+    # rounded below max / 127 (at most 127 s 2^-11)
+    assert np.all(np.abs(dec - x) <= s / 2 + np.maximum(amax - 127 * s, 0) + 1e-12)
+    # the largest element of every nonzero block reaches code +-127 or +-126 (f16 rounding of the scale)
+    big = np.abs(codes.reshape(50, 18, 32)).max(-1)
+    assert np.all((big >= 126) | (scales == 0))
+    # halves round away from zero: 0.5 and -1.5 steps with scale 1
+    xh = np.zeros(32)
+    xh[0], xh[1], xh[2] = 127.0, 0.5, -1.5
+    ch, sh = O.encode_q8_0(xh)
+    assert sh[0] == 1.0 and ch[:3].tolist() == [127, 1, -2]
+
+
 # ------------------------------------------------------------------ IndexShare --
 
 def test_index_share_rule_reproduces_the_page_counts():
