@@ -15,7 +15,8 @@ protocol (tiny prefill, batched decode, block-pooled chunk, long decode).
 --config n makes workload n the headline and times nothing else.  Beside the
 hot path it times the indexer-key cache write (rotate + fp8 quantise) at the
 long-decode cache shape, the incremental block pooling of one micro-batch,
-and an 8-layer IndexShare decode stack, reported under "next_rows".
+an 8-layer IndexShare decode stack, and decode attention over q8_0 latent
+rows against bf16 ones, reported under "next_rows".
 """
 
 import argparse
@@ -331,6 +332,70 @@ def index_share_row(dsa, inputs, torch, steps):
             "query_tokens_per_s": wl.S * wl.n_q / (ms_shared * 1e-3), "speedup": round(ms_own / ms_shared, 3)}
 
 
+# ------------------------------------------------ next row: q8_0 latent rows
+
+def q8_latent_row(dsa, inputs, torch, steps, flush):
+    """Decode attention over the latent rows cached as q8_0 against the same
+    rows in bf16, at the batched-decode (32 x 32768) and long-decode
+    (8 x 131072) shapes: the indexer's top-k of each workload selects the
+    rows, then attention alone is timed (dsa_sparse_attn: the gathered tile
+    kernel and the split merge), caches flushed before each call, HIP events
+    on the launch stream.  Algorithmic bytes: each selected row once (1152
+    bytes in bf16; 576 codes + 18 f16 scales = 612 in q8_0), the queries read
+    and the f32 outputs written; flops: 2 (576 + 512) per head and row."""
+    res = {}
+    for n in (3, 5):
+        wl = inputs.preset(n)
+        x = inputs.generate(wl, device="cuda")
+        sc = dsa.index_scores(x["q_idx"], x["k_idx"], x["w"], x["q_pos"], k_scale=x["k_scale"],
+                              kv_len=x["kv_len"], hadamard_q=wl.hadamard_q)
+        idx = dsa.topk(sc, x["q_pos"], wl.top_k, n_sink=wl.n_sink, kv_len=x["kv_len"])
+        del sc
+        codes, scales = inputs.q8_0_latent(x["K"])
+        out_b = torch.empty((wl.S, wl.n_q, wl.Hq, wl.Dv), device="cuda", dtype=torch.float32)
+        out_q = torch.empty_like(out_b)
+        kw = dict(kv_len=x["kv_len"], scale=wl.scale)
+
+        def bf16():
+            dsa.sparse_attn(x["Q"], x["K"], x["V"], x["q_pos"], idx, out=out_b, **kw)
+
+        def q8():
+            dsa.sparse_attn(x["Q"], codes, codes[..., :wl.Dv], x["q_pos"], idx, kv_scale=scales, out=out_q, **kw)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            ev = [(dsa.Event(), dsa.Event()) for _ in range(steps)]
+            for a, b in ev:
+                if flush is not None:
+                    flush.amax()
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            return sum(a.elapsed_ms(b) for a, b in ev) / steps
+
+        ms_b, ms_q = timed(bf16), timed(q8)
+        pairs = int((idx >= 0).sum().item())
+        io = wl.S * wl.n_q * wl.Hq * (wl.Dk * 2 + wl.Dv * 4)
+        by_b, by_q = pairs * 1152 + io, pairs * 612 + io
+        fl = 2.0 * pairs * wl.Hq * (wl.Dk + wl.Dv)
+        linf = float((out_q - out_b).abs().max() / out_b.abs().max())
+        res[wl.name] = {
+            "kernel": "attn_mla_q8_kernel", "attended_rows": pairs,
+            "ms_bf16": round(ms_b, 5), "ms_q8_0": round(ms_q, 5), "speedup": round(ms_b / ms_q, 3),
+            "bytes_bf16": by_b, "bytes_q8_0": by_q,
+            "hbm_frac_bf16": by_b / (ms_b * 1e-3) / PEAK_HBM, "hbm_frac_q8_0": by_q / (ms_q * 1e-3) / PEAK_HBM,
+            "mfma_frac_bf16": fl / (ms_b * 1e-3) / PEAK["bf16"], "mfma_frac_q8_0": fl / (ms_q * 1e-3) / PEAK["f16"],
+            "linf_rel_q8_vs_bf16": round(linf, 5),
+            "timing": "attention + split merge, caches flushed before each call" if flush is not None else "warm"}
+        print(f"bench: q8_0 latent rows, {wl.name}: bf16 {ms_b:.4f} ms, q8_0 {ms_q:.4f} ms", file=sys.stderr,
+              flush=True)
+        del x, codes, scales, idx, out_b, out_q
+        torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------- main
 
 def time_workload(dsa, inputs, torch, wl, steps, warmup, flush):
@@ -457,9 +522,12 @@ def main():
     from sparse_top_attention_indexer_amd import inputs
 
     if args.next_rows_only:
+        flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
         print(json.dumps({"next_rows": {"index_key_write": key_write_row(dsa, inputs, torch, 20),
                                         "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
-                                        "index_share": index_share_row(dsa, inputs, torch, 5)}}), flush=True)
+                                        "index_share": index_share_row(dsa, inputs, torch, 5),
+                                        "q8_0_latent": q8_latent_row(dsa, inputs, torch, 10, flush)}}),
+              flush=True)
         return
     headline = args.config if args.config is not None else 2
     # Before each timed step a 1 GiB read evicts the L2s and the 256 MB
@@ -505,7 +573,8 @@ def main():
     if not args.no_next_rows:
         line["next_rows"] = {"index_key_write": key_write_row(dsa, inputs, torch, 20),
                              "block_pool_update": pool_update_row(dsa, inputs, torch, 20),
-                             "index_share": index_share_row(dsa, inputs, torch, 5)}
+                             "index_share": index_share_row(dsa, inputs, torch, 5),
+                             "q8_0_latent": q8_latent_row(dsa, inputs, torch, 10, flush)}
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

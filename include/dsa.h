@@ -68,12 +68,15 @@
 extern "C" {
 #endif
 
-/* Element types. DSA_FP8_E4M3 is OCP float8 e4m3fn (max 448, no infinities). */
+/* Element types. DSA_FP8_E4M3 is OCP float8 e4m3fn (max 448, no infinities).
+ * DSA_Q8_0 is a storage format of MLA latent rows only: int8 codes with one
+ * f16 scale per 32 consecutive values (ggml's q8_0, held as two arrays). */
 typedef enum {
   DSA_F32 = 0,
   DSA_BF16 = 1,
   DSA_F16 = 2,
-  DSA_FP8_E4M3 = 3
+  DSA_FP8_E4M3 = 3,
+  DSA_Q8_0 = 4
 } dsa_dtype;
 
 /* Status codes. */
@@ -273,6 +276,20 @@ int32_t dsa_index_share_source(int32_t layer);
  *          n_kv * k_tok_stride * 2 < 2^32, and in block mode k_sel <= 1024
  *          (DSA_ERR_SHAPE otherwise);
  *  - GQA:  BF16, Dk == Dv == 128, Hq / Hkv <= 16.
+ * q8_0 latent rows ([QQ8] below): kv_format = DSA_Q8_0 with the MLA shapes
+ * (Q BF16): K = V = int8 codes (the strides count bytes), kv_scale = f16
+ * scales [S, n_kv, 18] contiguous, 16-byte aligned; every latent value is
+ * code x scale of its 32-value block.  Scores take that value exactly (as the
+ * sum of two f16 parts) against the query in f16 (each head scaled by a power
+ * of two, undone after); the value product takes it rounded to f16.  Values
+ * must lie in the f16 range (|code x scale| <= 65504, i.e. scales <= 515);
+ * larger ones give undefined outputs.  Errors: DSA_ERR_NULL without kv_scale,
+ * DSA_ERR_DTYPE for other Q types or formats, DSA_ERR_UNSUPPORTED for other
+ * shapes, DSA_ERR_ALIGN for a misaligned kv_scale or a row stride not a
+ * multiple of 16 bytes.
+ *  - [QQ8]  ik_llama_opt log, openPangu port, "Add OpenPangu q8_0 latent
+ *           cache type": MLA latent rows cached as q8_0 (0.53x the bytes of
+ *           f16), read back by attention.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const void* q;          /* [S, n_q, Hq, Dk] contiguous                        */
@@ -289,7 +306,8 @@ typedef struct {
   int32_t k_sel;          /* entries per idx row (ignored when idx == NULL)     */
   int32_t c;              /* >= 1; block mode when > 1                          */
   float scale;            /* softmax scale; <= 0 selects 1/sqrt(Dk)             */
-  int32_t pad_;           /* reserved, set to 0                                 */
+  int32_t kv_format;      /* 0 (K/V of dtype) or DSA_Q8_0 (MLA latent rows)     */
+  const void* kv_scale;   /* [S, n_kv, Dk / 32] f16 iff kv_format == DSA_Q8_0   */
 } dsa_attn_desc;
 
 /* Workspace for dsa_sparse_attn; dense != 0 sizes the idx == NULL call. */
@@ -324,7 +342,7 @@ typedef struct {
   int32_t a_dtype, o_dtype;
   int32_t Hq, Hkv, Dk, Dv;
   float scale;
-  int32_t pad_;
+  int32_t kv_format;      /* as in dsa_attn_desc                                */
   /* shared */
   int32_t S, n_q;
   int64_t n_kv;
@@ -337,6 +355,7 @@ typedef struct {
   /* optional timing: NULL, or DSA_N_PHASE_EVENTS hipEvent_t handles recorded
    * on the stream at the phase boundaries */
   void* const* phase_events;
+  const void* kv_scale;   /* as in dsa_attn_desc                                */
 } dsa_forward_desc;
 
 size_t dsa_forward_workspace_bytes(const dsa_forward_desc* d);

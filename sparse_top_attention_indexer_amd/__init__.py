@@ -24,6 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.float8_e4m3fn: 3}
+Q8_0 = 4   # q8_0 latent rows: int8 codes + f16 scales per 32 values
 
 
 class DsaError(RuntimeError):
@@ -52,7 +53,8 @@ class AttnDesc(ctypes.Structure):
                 ("v_seq_stride", _i64), ("v_tok_stride", _i64), ("v_head_stride", _i64),
                 ("q_pos", _vp), ("kv_len", _vp), ("dtype", _i32), ("o_dtype", _i32),
                 ("S", _i32), ("n_q", _i32), ("Hq", _i32), ("Hkv", _i32), ("Dk", _i32), ("Dv", _i32),
-                ("n_kv", _i64), ("k_sel", _i32), ("c", _i32), ("scale", ctypes.c_float), ("pad_", _i32)]
+                ("n_kv", _i64), ("k_sel", _i32), ("c", _i32), ("scale", ctypes.c_float), ("kv_format", _i32),
+                ("kv_scale", _vp)]
 
 
 class ForwardDesc(ctypes.Structure):
@@ -63,9 +65,9 @@ class ForwardDesc(ctypes.Structure):
                 ("k_seq_stride", _i64), ("k_tok_stride", _i64), ("k_head_stride", _i64),
                 ("v_seq_stride", _i64), ("v_tok_stride", _i64), ("v_head_stride", _i64),
                 ("a_dtype", _i32), ("o_dtype", _i32), ("Hq", _i32), ("Hkv", _i32), ("Dk", _i32),
-                ("Dv", _i32), ("scale", ctypes.c_float), ("pad_", _i32),
+                ("Dv", _i32), ("scale", ctypes.c_float), ("kv_format", _i32),
                 ("S", _i32), ("n_q", _i32), ("n_kv", _i64), ("q_pos", _vp), ("kv_len", _vp),
-                ("out", _vp), ("idx_out", _vp), ("scores_out", _vp), ("phase_events", _vp)]
+                ("out", _vp), ("idx_out", _vp), ("scores_out", _vp), ("phase_events", _vp), ("kv_scale", _vp)]
 
 
 SYMBOLS = {
@@ -251,27 +253,41 @@ def _strides(t):
     return t.stride(0), t.stride(1), t.stride(2)
 
 
-def _attn_desc(Q, K, V, q_pos, kv_len, k_sel, c, scale, o_dtype):
+def _kv_format(K, kv_scale):
+    """(kv_format, scale pointer): q8_0 when the latent rows are int8 codes."""
+    if K.dtype == torch.int8:
+        if kv_scale is None or kv_scale.dtype != torch.float16 or not kv_scale.is_contiguous():
+            raise DsaError("q8_0 latent rows need kv_scale: contiguous f16 [S, n_kv, Dk // 32]")
+        return Q8_0, _ptr(kv_scale)
+    if kv_scale is not None:
+        raise DsaError("kv_scale is only for int8 (q8_0) latent rows")
+    return 0, None
+
+
+def _attn_desc(Q, K, V, q_pos, kv_len, k_sel, c, scale, o_dtype, kv_scale=None):
     S, n_q, Hq, Dk = Q.shape
     _, n_kv, Hkv, _ = K.shape
     Dv = V.shape[3]
     ks, vs = _strides(K), _strides(V)
+    fmt, sc = _kv_format(K, kv_scale)
     return AttnDesc(_ptr(Q), _ptr(K), _ptr(V), ks[0], ks[1], ks[2], vs[0], vs[1], vs[2],
                     _ptr(_i32c(q_pos)), _ptr(_i32c(kv_len)), _dt(Q), DTYPES[o_dtype],
-                    S, n_q, Hq, Hkv, Dk, Dv, n_kv, k_sel, c, 0.0 if scale is None else float(scale), 0)
+                    S, n_q, Hq, Hkv, Dk, Dv, n_kv, k_sel, c, 0.0 if scale is None else float(scale), fmt, sc)
 
 
 def sparse_attn(Q, K, V, q_pos, idx=None, *, c: int = 1, kv_len=None, scale=None,
-                o_dtype=torch.float32, out=None):
-    """Attention over the selected tokens (idx None = dense causal): [S, n_q, Hq, Dv]."""
-    _need_gpu(Q, K, V, q_pos, idx, kv_len)
+                o_dtype=torch.float32, out=None, kv_scale=None):
+    """Attention over the selected tokens (idx None = dense causal): [S, n_q, Hq, Dv].
+    q8_0 latent rows: K int8 codes [S, n_kv, 1, 576], V = K[..., :512], and
+    kv_scale f16 [S, n_kv, 18]."""
+    _need_gpu(Q, K, V, q_pos, idx, kv_len, kv_scale)
     Q = Q.contiguous()
     S, n_q, Hq, _ = Q.shape
     Dv = V.shape[3]
     k_sel = 0 if idx is None else idx.shape[2]
     if idx is not None:
         idx = _i32c(idx.contiguous())
-    d = _attn_desc(Q, K, V, q_pos, kv_len, k_sel, c, scale, o_dtype)
+    d = _attn_desc(Q, K, V, q_pos, kv_len, k_sel, c, scale, o_dtype, kv_scale)
     if out is None:
         out = torch.empty((S, n_q, Hq, Dv), device=Q.device, dtype=o_dtype)
     nbytes = lib().dsa_sparse_attn_workspace_bytes(ctypes.byref(d), int(idx is None))
@@ -304,28 +320,29 @@ class Event:
 
 
 def _forward_desc(Q, K, V, q_idx, k_idx, w, top_k, c, q_pos, k_scale, n_sink, scale, hadamard_q,
-                  kv_len, out, idx_out, scores_out, events_arr):
+                  kv_len, out, idx_out, scores_out, events_arr, kv_scale=None):
     S, n_q, Hq, Dk = Q.shape
     _, n_kv, Hkv, _ = K.shape
     Dv = V.shape[3]
     H, D = q_idx.shape[2], q_idx.shape[3]
     ks, vs = _strides(K), _strides(V)
+    fmt, sc = _kv_format(K, kv_scale)
     return ForwardDesc(_ptr(q_idx), _ptr(k_idx), _ptr(k_scale), _ptr(w), _dt(q_idx), _dt(k_idx), H, D,
                        top_k, c, n_sink, int(hadamard_q), _ptr(Q), _ptr(K), _ptr(V),
                        ks[0], ks[1], ks[2], vs[0], vs[1], vs[2], _dt(Q), DTYPES[out.dtype], Hq, Hkv, Dk, Dv,
-                       0.0 if scale is None else float(scale), 0, S, n_q, n_kv,
+                       0.0 if scale is None else float(scale), fmt, S, n_q, n_kv,
                        _ptr(_i32c(q_pos)), _ptr(_i32c(kv_len)), _ptr(out), _ptr(idx_out), _ptr(scores_out),
-                       None if events_arr is None else ctypes.cast(events_arr, ctypes.c_void_p))
+                       None if events_arr is None else ctypes.cast(events_arr, ctypes.c_void_p), sc)
 
 
 def forward_workspace_bytes(Q, K, V, q_idx, k_idx, w, top_k, compress_ratio, q_pos, *, k_scale=None,
                             n_sink=0, scale=None, hadamard_q=False, kv_len=None, o_dtype=torch.float32,
-                            return_idx=False, return_scores=False) -> int:
+                            return_idx=False, return_scores=False, kv_scale=None) -> int:
     S, n_q, Hq, _ = Q.shape
     out = torch.empty(0, dtype=o_dtype)
     dummy = ctypes.c_void_p(16)
     d = _forward_desc(Q, K, V, q_idx, k_idx, w, top_k, compress_ratio, q_pos, k_scale, n_sink, scale,
-                      hadamard_q, kv_len, out, None, None, None)
+                      hadamard_q, kv_len, out, None, None, None, kv_scale)
     d.out = dummy
     if return_idx:
         d.idx_out = dummy
@@ -337,9 +354,11 @@ def forward_workspace_bytes(Q, K, V, q_idx, k_idx, w, top_k, compress_ratio, q_p
 def forward(Q, K, V, q_idx, k_idx, w, top_k: int, compress_ratio: int, q_pos, *, k_scale=None,
             n_sink: int = 0, scale=None, hadamard_q: bool = False, kv_len=None, out=None,
             o_dtype=torch.float32, return_idx: bool = False, return_scores: bool = False,
-            workspace: Optional[torch.Tensor] = None, phase_events: Optional[Sequence[Event]] = None):
-    """The whole path (dsa_forward): O [S, n_q, Hq, Dv], plus idx / scores if asked."""
-    _need_gpu(Q, K, V, q_idx, k_idx, w, q_pos, k_scale, kv_len)
+            workspace: Optional[torch.Tensor] = None, phase_events: Optional[Sequence[Event]] = None,
+            kv_scale=None):
+    """The whole path (dsa_forward): O [S, n_q, Hq, Dv], plus idx / scores if asked.
+    q8_0 latent rows as in sparse_attn (K int8 codes, kv_scale f16)."""
+    _need_gpu(Q, K, V, q_idx, k_idx, w, q_pos, k_scale, kv_len, kv_scale)
     S, n_q, Hq, _ = Q.shape
     Dv = V.shape[3]
     n_kv = K.shape[1]
@@ -355,7 +374,7 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, compress_ratio: int, q_pos, *,
     if phase_events is not None:
         events_arr = (ctypes.c_void_p * 5)(*[e.handle.value for e in phase_events])
     d = _forward_desc(Q, K, V, q_idx, k_idx, w, top_k, c, q_pos, k_scale, n_sink, scale, hadamard_q,
-                      kv_len, out, idx_out, scores_out, events_arr)
+                      kv_len, out, idx_out, scores_out, events_arr, kv_scale)
     nbytes = int(lib().dsa_forward_workspace_bytes(ctypes.byref(d)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), device=Q.device, dtype=torch.uint8)

@@ -66,6 +66,15 @@ int check_topk(const float* scores, const dsa_topk_desc* d, const int32_t* idx) 
 
 // Attention family of a descriptor, or a negative status.
 int attn_family(const dsa_attn_desc* d) {
+  if (d->kv_format != 0 && d->kv_format != d->dtype && d->kv_format != DSA_Q8_0) return DSA_ERR_DTYPE;
+  if (d->kv_format == DSA_Q8_0) {   // q8_0 latent rows: the MLA shapes only, byte strides
+    if (d->dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (d->Hkv == 1 && d->Dk == 576 && d->Dv == 512 && d->Hq % 16 == 0 && d->v == d->k &&
+        d->v_seq_stride == d->k_seq_stride && d->v_tok_stride == d->k_tok_stride &&
+        d->n_kv * d->k_tok_stride < (int64_t(1) << 32))
+      return ATTN_MLA;
+    return DSA_ERR_UNSUPPORTED;
+  }
   if (d->dtype == DSA_F32) {
     if (d->Dk > 256 || d->Dv > 256) return DSA_ERR_UNSUPPORTED;
     return ATTN_F32;
@@ -93,8 +102,10 @@ int check_attn(const dsa_attn_desc* d, const int32_t* idx, const void* out) {
   const int fam = attn_family(d);
   if (fam < 0) return fam;
   if (fam == ATTN_MLA && idx && d->c > 1 && d->k_sel > MLA_MAX_BLOCKS) return DSA_ERR_SHAPE;
-  if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(out)) return DSA_ERR_ALIGN;
-  const size_t es = esize(d->dtype);
+  if (d->kv_format == DSA_Q8_0 && !d->kv_scale) return DSA_ERR_NULL;
+  if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(out) || !aligned16(d->kv_scale))
+    return DSA_ERR_ALIGN;
+  const size_t es = d->kv_format == DSA_Q8_0 ? 1 : esize(d->dtype);
   if (fam != ATTN_F32) {
     const int64_t strides[6] = {d->k_seq_stride, d->k_tok_stride, d->k_head_stride,
                                 d->v_seq_stride, d->v_tok_stride, d->v_head_stride};
@@ -133,6 +144,8 @@ AttnParams attn_params(const dsa_attn_desc* d, const int32_t* idx, void* out) {
   const float scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf(static_cast<float>(d->Dk));
   p.scale_log2 = scale * 1.4426950408889634f;
   p.family = attn_family(d);
+  p.kq8 = d->kv_format == DSA_Q8_0 ? 1 : 0;
+  p.k_scale = p.kq8 ? d->kv_scale : nullptr;
   int64_t list_len = d->n_kv;
   if (idx) list_len = d->c > 1 ? static_cast<int64_t>(d->k_sel) * d->c + d->c - 1 : d->k_sel;
   attn_plan(p, list_len);
@@ -416,6 +429,8 @@ int plan_forward(const dsa_forward_desc* d, ForwardPlan* f) {
   ad.k_sel = f->k_out;
   ad.c = d->c;
   ad.scale = d->scale;
+  ad.kv_format = d->kv_format;
+  ad.kv_scale = d->kv_scale;
   {
     static const int32_t dummy_idx[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
     const int st = check_attn(&ad, dummy_idx, d->out);

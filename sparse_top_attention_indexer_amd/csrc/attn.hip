@@ -625,6 +625,374 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   if (grp == 1) write_out();
 }
 
+// ========================================================= MLA, q8_0 rows ==
+
+// The latent rows as q8_0 (ik_llama_opt log, openPangu port, "Add OpenPangu
+// q8_0 latent cache type": int8 codes, one f16 scale per 32 values; 612 bytes
+// a row against 1152 in bf16).  Layout: codes [S, n_kv, 576] int8 at the K
+// strides (bytes), scales [S, n_kv, 18] f16, contiguous.
+//
+// Precision.  A dequantised value c s (a 7-bit code times an 11-bit scale)
+// carries up to 18 significant bits: bf16 (8) or f16 (11) alone would lose
+// the score accuracy of bf16 rows (rows with outliers magnify a key error
+// through the softmax).  Scores take it exactly, as the sum of hi = f16(c s)
+// and lo = c s - hi (the residual is a multiple of the scale's last bit below
+// half an ulp of hi: an f16 value, exact).  Queries enter as f16, each head's
+// scaled by the power of two that puts its largest component in [2^14, 2^15)
+// (exact for components down to 2^-24 of the largest); the factor is folded
+// back into that head's softmax scale and running max.  Values take hi alone
+// (relative error 2^-12), the weights f16 with attn_mla_kernel's residual
+// rule.  The dequantised values must lie in the f16 range (|c s| <= 65504,
+// so scales up to 515).
+constexpr int Q8_BLOCKS = MLA_DK / 32;                     // scales per row
+constexpr int Q8_STAGE = TILE * MLA_DK;                    // one tile's codes (18 KB)
+// one tile's scales: 9 dwords a row, 288 in all, loaded by 5 whole waves
+// (each lane writes its own dword; the last 32 lanes' land past the 288)
+constexpr int Q8_SSTAGE = (TILE * 9 + 63) / 64 * 256;
+// tile of hi values, tile of lo values (attn_mla_kernel's layout each), code
+// and scale staging, token ids of three tiles
+constexpr size_t MLA_Q8_LDS = 2 * KT_BYTES + Q8_STAGE + Q8_SSTAGE + 3 * TILE * 4 + 64 + MLA_MAX_BLOCKS * 4;
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// One lane-wide global -> LDS load of 4 bytes (lane L: lds_base + 4 L), as dma16.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// 16 codes (4 per dword) and their f16 scale s -> hi = f16(c s) and
+// lo = f16(c s - hi), 8 dims per u32x4 (h0, l0: dims 0..7; h1, l1: 8..15).
+// A code byte c, offset to c + 128 and placed under the f16 exponent of 1024,
+// reads as 1024 + c + 128; taking 1152 off gives c exactly.  The product is
+// rounded once, and the fused residual is exact.
+__device__ __forceinline__ void q8_split16(u32x4_t c, uint16_t sbits, u32x4_t& h0, u32x4_t& h1, u32x4_t& l0,
+                                           u32x4_t& l1) {
+#pragma clang fp contract(off)
+  const _Float16 sh = __builtin_bit_cast(_Float16, sbits);
+  const f16x2_t s2 = {sh, sh};
+  const f16x2_t bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i] ^ 0x80808080u;
+    const uint32_t e[2] = {__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),    // codes 0, 1
+                           __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)};   // codes 2, 3
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f16x2_t cv = __builtin_bit_cast(f16x2_t, e[j]) - bias;
+      const f16x2_t hv = cv * s2;
+      const f16x2_t lv = __builtin_elementwise_fma(cv, s2, -hv);
+      h[2 * i + j] = __builtin_bit_cast(uint32_t, hv);
+      l[2 * i + j] = __builtin_bit_cast(uint32_t, lv);
+    }
+  }
+  h0 = u32x4_t{h[0], h[1], h[2], h[3]};
+  h1 = u32x4_t{h[4], h[5], h[6], h[7]};
+  l0 = u32x4_t{l[0], l[1], l[2], l[3]};
+  l1 = u32x4_t{l[4], l[5], l[6], l[7]};
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
+// One workgroup = one query row x one stream chunk x 128 heads, 8 waves of 16
+// heads, as attn_mla_kernel, for q8_0 latent rows.  Per tile of 32 stream
+// entries: the codes and scales of the next tile go straight to LDS staging
+// areas (direct global -> LDS loads) while the tile in LDS is computed; after
+// the barrier that ends the tile's products they are split into hi and lo
+// f16 tiles (see above) over it, and a second barrier completes them.
+// Scores run on f16 MFMAs over hi and lo (72 per wave and tile), the PV
+// products over hi with f16 weights; the contraction order, the online
+// softmax (lazy running max, weights plus their residual on tiles where one
+// weight is large against the normaliser) and the output follow
+// attn_mla_kernel, in one wave group.  Token ids of tile u + 2 are fetched
+// during tile u.
+__global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_q8_kernel(AttnParams p) {
+  constexpr int NW = MLA_WAVES;
+  extern __shared__ __align__(16) uint8_t s_raw[];
+  uint8_t* s_kb = s_raw;                                                     // hi tile, then lo tile
+  uint8_t* s_st = s_raw + 2 * KT_BYTES;                                     // code staging (Q8_STAGE)
+  const uint16_t* s_ss = reinterpret_cast<const uint16_t*>(s_st + Q8_STAGE); // scale staging: row r at 18 r
+  int32_t* s_tk = reinterpret_cast<int32_t*>(s_st + Q8_STAGE + Q8_SSTAGE);  // token ids of 3 tiles
+  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_tk + 3 * TILE);
+  int32_t* s_blk = reinterpret_cast<int32_t*>(s_scr + 16);                  // MLA_MAX_BLOCKS
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const int64_t row = rows - 1 - blockIdx.x / p.n_split;   // latest (longest causal) rows first
+  const int sp = blockIdx.x % p.n_split;
+  const int s = static_cast<int>(row / p.n_q);
+  const int col = lane & 15, q = lane >> 4;
+  const int head0 = blockIdx.y * (16 * NW) + wid * 16;
+  const bool wvalid = head0 < p.Hq;
+  const int head = head0 + col;
+
+  // Q^T fragments in attn_mla_kernel's permutation (a wave without heads
+  // loads head 0's query; its outputs are never written), as f16 of the
+  // query times 2^qk, qk from the head's largest |component| (the four
+  // lanes col + 16 q hold all 576 dims of head col)
+  u32x4_t qf[18];
+  int qk;
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (row * p.Hq + (wvalid ? head : 0)) * MLA_DK;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int chunk = ks < 16 ? 16 * (ks >> 2) + 4 * q + (ks & 3) : 64 + 2 * q + (ks - 16);
+      qf[ks] = *reinterpret_cast<const u32x4_t*>(qr + 8 * chunk);
+    }
+    uint32_t m = 0;   // largest bf16 magnitude (bits), monotone in the value
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max(qf[ks][i] & 0x7fffu, (qf[ks][i] >> 16) & 0x7fffu));
+    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, 64)));
+    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, 64)));
+    // largest component 2^E (1 + f), E = (m >> 7) - 127: scale by 2^(14 - E)
+    qk = m == 0 ? 0 : min(141 - static_cast<int>(m >> 7), 64);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      u32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = pack_h2(__builtin_amdgcn_ldexpf(__uint_as_float(qf[ks][i] << 16), qk),
+                       __builtin_amdgcn_ldexpf(__uint_as_float(qf[ks][i] & 0xffff0000u), qk));
+      qf[ks] = v;
+    }
+  }
+  const float c2 = __builtin_amdgcn_ldexpf(p.scale_log2, -qk);   // scores arrive times 2^qk
+  const StreamInfo si = stream_setup<NW>(p, row, s_blk, s_scr);
+  int64_t p0, p1;
+  split_range(p, sp, si.len, &p0, &p1);
+  const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
+
+  const int8_t* kseq = static_cast<const int8_t*>(p.k) + s * p.k_seq;
+  const uint16_t* sseq = static_cast<const uint16_t*>(p.k_scale) + static_cast<int64_t>(s) * p.n_kv * Q8_BLOCKS;
+  // token id of stream entry r of tile u (-1: dead or past the chunk); tile
+  // v's ids sit in s_tk[v % 3], written by wave 0 one tile ahead of the loads
+  auto tok = [&](int u, int r) __attribute__((always_inline)) -> int32_t {
+    const int64_t pos = p0 + static_cast<int64_t>(u) * TILE + r;
+    return pos < p1 ? static_cast<int32_t>(stream_token(p, row, si, s_blk, pos)) : -1;
+  };
+  // The codes and scales of a tile go straight to LDS staging areas (direct
+  // global -> LDS loads; no registers held across the products): code chunk c
+  // (16 bytes) at 16 c, in the order main chunks t (rows t / 32, dims
+  // 16 (t % 32) ..) and t + 512 (rows + 16), then rope chunks 1024 + t (t <
+  // 128: row t / 4, dims 512 + 16 (t % 4) ..); scale dword d of row r (the
+  // row's 18 scales are 9 dwords) at 4 (9 r + d).  Wave w, load i, lane L
+  // fetches chunk 512 i + 64 w + L.  Dead entries read row 0 (their weights
+  // are zero).
+  const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sseq);
+  const uint32_t st_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_st));
+  const uint32_t pitch = static_cast<uint32_t>(p.k_tok);   // bytes per latent row
+  auto load_stage = [&](int u) __attribute__((always_inline)) {
+    int t = tid;
+    asm volatile("" : "+v"(t));   // addresses from tid at each use, not held across the loop
+    const int32_t* tk = s_tk + (u % 3) * TILE;
+    const int32_t a = tk[t >> 5], b = tk[(t >> 5) + 16], r = tk[(t >> 2) & 31];
+    const uint32_t ta = a > 0 ? a : 0, tb = b > 0 ? b : 0, tr = r > 0 ? r : 0;
+    const uint32_t c = t & 31, rcc = t & 3;
+    dma16(kseq, ta * pitch + 16u * c, __builtin_amdgcn_readfirstlane(st_lds + 1024u * wid));
+    dma16(kseq, tb * pitch + 16u * c, __builtin_amdgcn_readfirstlane(st_lds + 1024u * (8 + wid)));
+    if (wid < 2) dma16(kseq, tr * pitch + 512u + 16u * rcc, __builtin_amdgcn_readfirstlane(st_lds + 1024u * (16 + wid)));
+    if (wid < (TILE * 9 + 63) / 64) {   // 288 scale dwords
+      const int d = (t < TILE * 9 ? t : TILE * 9 - 1), sr = d / 9, sj = d % 9;
+      const int32_t ts = tk[sr];
+      const uint32_t tsu = ts > 0 ? ts : 0;
+      dma4(sbytes, tsu * (Q8_BLOCKS * 2u) + 4u * sj, __builtin_amdgcn_readfirstlane(st_lds + Q8_STAGE + 256u * wid));
+    }
+  };
+  // the staged tile, split, into the hi and lo tiles: main row r keeps its
+  // 16-byte chunk c (dims 8 c ..) in slot c ^ main_swz(r), rope row r its
+  // chunk c in slot c ^ rope_swz(r)
+  auto store_stage = [&]() __attribute__((always_inline)) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int ra = t >> 5, c = t & 31, rb = ra + 16, rw = (t >> 2) & 31, rcc = t & 3;
+    u32x4_t h0, h1, l0, l1;
+    auto put = [&](uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4_t*>(s_kb + o0) = h0;
+      *reinterpret_cast<u32x4_t*>(s_kb + o1) = h1;
+      *reinterpret_cast<u32x4_t*>(s_kb + KT_BYTES + o0) = l0;
+      *reinterpret_cast<u32x4_t*>(s_kb + KT_BYTES + o1) = l1;
+    };
+    q8_split16(*reinterpret_cast<const u32x4_t*>(s_st + 16 * t), s_ss[Q8_BLOCKS * ra + (c >> 1)], h0, h1, l0, l1);
+    put(ra * 1024 + 16 * ((2 * c) ^ main_swz(ra)), ra * 1024 + 16 * ((2 * c + 1) ^ main_swz(ra)));
+    q8_split16(*reinterpret_cast<const u32x4_t*>(s_st + 16 * (512 + t)), s_ss[Q8_BLOCKS * rb + (c >> 1)], h0, h1, l0,
+               l1);
+    put(rb * 1024 + 16 * ((2 * c) ^ main_swz(rb)), rb * 1024 + 16 * ((2 * c + 1) ^ main_swz(rb)));
+    if (wid < 2) {
+      q8_split16(*reinterpret_cast<const u32x4_t*>(s_st + 16 * (1024 + t)), s_ss[Q8_BLOCKS * rw + 16 + (rcc >> 1)],
+                 h0, h1, l0, l1);
+      put(KT_MAIN + rw * 128 + 16 * ((2 * rcc) ^ rope_swz(rw)), KT_MAIN + rw * 128 + 16 * ((2 * rcc + 1) ^ rope_swz(rw)));
+    }
+  };
+
+  f32x4_t o[32];
+#pragma unroll
+  for (int db = 0; db < 32; ++db) o[db] = f32x4_t{};
+  float m_run = NEG_INF, l_run = 0.f;
+
+  // K fragment of key block mb, contraction step ks (attn_mla_kernel's
+  // addressing; + KT_BYTES for the lo tile)
+  const uint32_t cs = col * 1024u + ((64u * q) ^ (16u * main_swz(col)));
+  const uint32_t cr = KT_MAIN + col * 128u + ((32u * q) ^ (16u * rope_swz(col)));
+  auto scores = [&](f32x4_t& s0, f32x4_t& s1) __attribute__((always_inline)) {
+    uint32_t xs = cs, xr = cr;
+    asm volatile("" : "+v"(xs), "+v"(xr));
+    auto frag = [&](int i) __attribute__((always_inline)) -> u32x4_t {
+      const int ks = i >> 2, mb = (i >> 1) & 1, lo = i & 1;
+      const uint8_t* ad = ks < 16 ? s_kb + (xs ^ (16u * (ks & 3))) + 256 * (ks >> 2) + 16384 * mb
+                                  : s_kb + (xr ^ (16u * (ks - 16))) + 2048 * mb;
+      return *reinterpret_cast<const u32x4_t*>(ad + lo * KT_BYTES);
+    };
+    constexpr int SD = 2;   // K fragments read ahead
+    u32x4_t kf[SD];
+#pragma unroll
+    for (int i = 0; i < SD; ++i) kf[i] = frag(i);
+    s0 = f32x4_t{};
+    s1 = f32x4_t{};
+    // product i: step i / 4, key block (i / 2) & 1, hi (i even) or lo
+#pragma unroll
+    for (int i = 0; i < 72; ++i) {
+      if ((i >> 1) & 1) s1 = mfma16x16x32_f16(kf[i % SD], qf[i >> 2], s1);
+      else s0 = mfma16x16x32_f16(kf[i % SD], qf[i >> 2], s0);
+      if (i + SD < 72) kf[i % SD] = frag(i + SD);
+    }
+  };
+  // online softmax of the tile (attn_mla_kernel's rule, f16 weights);
+  // returns the factor that rescales what was accumulated before
+  auto softmax = [&](f32x4_t s0, f32x4_t s1, uint32_t live, u32x4_t& ph, u32x4_t& pl,
+                     bool& need_lo) __attribute__((always_inline)) -> float {
+    if (live != 0xffffffffu) {
+      const uint32_t lm = live >> (4 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!((lm >> j) & 1u)) s0[j] = NEG_INF;
+        if (!((lm >> (16 + j)) & 1u)) s1[j] = NEG_INF;
+      }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    tmax = quad_max(tmax);
+    const bool first = m_run == NEG_INF;
+    const bool grow = !first && (tmax - m_run) * c2 > 8.f;
+    const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
+    const float alpha = grow ? a : 1.f;
+    m_run = (first || grow) ? tmax : m_run;
+    const float mb = m_run == NEG_INF ? 0.f : m_run * c2;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -mb));
+      x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb));
+    }
+    uint32_t hv[4], lv[4];
+    float psum = 0.f, hsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hv[i] = pack_h2(x[2 * i], x[2 * i + 1]);
+      const f16x2_t hh = __builtin_bit_cast(f16x2_t, hv[i]);
+      const float h0 = static_cast<float>(hh.x), h1 = static_cast<float>(hh.y);
+      lv[i] = pack_h2(x[2 * i] - h0, x[2 * i + 1] - h1);
+      psum += x[2 * i] + x[2 * i + 1];
+      hsum += h0 + h1;
+    }
+    ph = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+    pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+    const float la = l_run * alpha, l_full = la + quad_sum(psum);
+    const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));
+    need_lo = __ballot(xmax > LO_SHARE * l_full) != 0;
+    l_run = need_lo ? l_full : la + quad_sum(hsum);
+    return alpha;
+  };
+  uint32_t cv;
+  {
+    const uint32_t m4 = (lane >> 2) & 3, r4 = lane & 3, R = 4 * q + m4, f = main_swz(R);
+    cv = R * 1024 + 16 * ((r4 >> 1) ^ (f & 1)) + 16 * (f & 14) + 8 * (r4 & 1);
+  }
+  constexpr int VD = 2;   // V^T fragments read ahead
+  auto pv = [&](const u32x4_t& pw) __attribute__((always_inline)) {
+    uint32_t x1 = cv;
+    asm volatile("" : "+v"(x1));
+    auto vfrag = [&](int db) __attribute__((always_inline)) -> u32x4_t {
+      uint8_t* ad = s_kb + (x1 ^ (32u * (db & 7))) + 256 * (db >> 3);
+      const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)ad);
+      const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(ad + 16384));
+      const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+      return u32x4_t{a2.x, a2.y, b2.x, b2.y};
+    };
+    u32x4_t vf[VD];
+#pragma unroll
+    for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      o[db] = mfma16x16x32_f16(vf[db % VD], pw, o[db]);
+      if (db + VD < 32) vf[db % VD] = vfrag(db + VD);
+    }
+  };
+
+  // prologue: token ids of tiles 0 and 1, tile 0 split into the tiles
+  if (wid == 0) s_tk[lane] = tok(lane >> 5, lane & 31);   // tiles 0 and 1 (entries past the chunk: -1)
+  __syncthreads();
+  if (n_tiles > 0) load_stage(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's staging loads have landed
+  __syncthreads();
+  if (n_tiles > 0) store_stage();
+  __syncthreads();
+  for (int u = 0; u < n_tiles; ++u) {
+    // the codes and scales of tile u + 1 and the token ids of tile u + 2 are
+    // in flight during the products of tile u; then, after a barrier, tile
+    // u + 1 is split over tile u
+    const bool more = u + 1 < n_tiles;
+    if (more) load_stage(u + 1);
+    int32_t t2 = -1;
+    if (wid == 0 && lane < 32) t2 = tok(u + 2, lane);
+    const uint32_t live = static_cast<uint32_t>(__ballot(s_tk[(u % 3) * TILE + (lane & 31)] >= 0));
+    f32x4_t s0, s1;
+    u32x4_t ph, pl;
+    bool need_lo;
+    scores(s0, s1);
+    const float alpha = softmax(s0, s1, live, ph, pl, need_lo);
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) o[db] *= alpha;
+    }
+    u32x4_t pw = ph;
+#pragma clang loop unroll(disable)
+    for (int ps = 0; ps < 1 + need_lo; ++ps) {
+      pv(pw);
+      pw = pl;
+    }
+    if (wid == 0 && lane < 32) s_tk[((u + 2) % 3) * TILE + lane] = t2;   // over tile u - 1's ids
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's staging loads have landed
+    __syncthreads();                      // all of the staging, the ids of tile u + 2; tile u read
+    if (more) store_stage();
+    __syncthreads();                      // tile u + 1 complete; the staging is free
+  }
+
+  // output (accumulator (db, j) holds dim 16 db + 4 q + j of head `head`)
+  if (!(wvalid && head < p.Hq)) return;
+  if (p.n_split == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * q;
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+      store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+  } else {
+    float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(MLA_DV);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
+    if (q == 0) {
+      pp[MLA_DV] = __builtin_amdgcn_ldexpf(m_run, -qk);   // the running max in score units
+      pp[MLA_DV + 1] = l_run;
+    }
+  }
+}
+
 // ============================================================== GQA kernel ==
 
 constexpr int GQA_D = 128;
@@ -1069,7 +1437,14 @@ size_t attn_workspace_bytes(const AttnParams& p) {
 hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t before_combine) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   hipError_t e;
-  if (p.family == ATTN_MLA) {
+  if (p.family == ATTN_MLA && p.kq8) {
+    // set on every call (the same value each time, no state kept between calls)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mla_q8_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_Q8_LDS));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_mla_q8_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hq + 127) / 128),
+                       dim3(64 * MLA_WAVES), MLA_Q8_LDS, st, p);
+  } else if (p.family == ATTN_MLA) {
     // set on every call (the same value each time, no state kept between calls)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mla_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_LDS));

@@ -65,6 +65,10 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4_t mfma16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
 
 // Packs two floats as bf16 (low half = a) / f16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

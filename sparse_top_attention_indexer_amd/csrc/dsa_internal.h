@@ -101,6 +101,7 @@ struct AttnParams {
   const int32_t* idx;    // null = dense
   void* out;
   float* part;           // split partials [rows][n_split][Hq][part_width(Dv)]: o, then m and l
+  const void* k_scale;   // q8_0 latent rows: f16 scales [S, n_kv, Dk / 32] (kq8), else null
   int32_t dtype, o_dtype;
   int32_t S, n_q, Hq, Hkv, Dk, Dv;
   int64_t n_kv;
@@ -110,6 +111,7 @@ struct AttnParams {
   int32_t n_split;       // key-stream splits per row
   int32_t split_len;     // stream entries per split (multiple of 32)
   int32_t family;        // ATTN_F32 / ATTN_MLA / ATTN_GQA
+  int32_t kq8;           // MLA: the latent rows are q8_0 codes (int8) with f16 block scales
 };
 enum { ATTN_F32 = 0, ATTN_MLA = 1, ATTN_GQA = 2 };
 // Block-mode list length (blocks per row) the MLA kernel keeps in LDS.

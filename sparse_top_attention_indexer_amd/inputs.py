@@ -224,3 +224,18 @@ def raw_key_batch(S: int, n_kv: int, D: int = 128, dtype=torch.bfloat16, seed: i
     block-pooled workload stores them."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     return torch.randn((S, n_kv, D), generator=g).to(dtype)
+
+
+def q8_0_latent(latent: torch.Tensor):
+    """The MLA latent rows [S, n_kv, 1, D] (D a multiple of 32) cached as q8_0,
+    the quantised latent cache type: codes int8 [S, n_kv, 1, D] and scales
+    f16 [S, n_kv, D / 32], one per block of 32 values (scale = f16(max |x| /
+    127), code = x / scale rounded half away from zero).  This is the cache
+    write that precedes attention; the values come from the seeded latent."""
+    S, n, h, D = latent.shape
+    x = latent.float().reshape(S, n, D // 32, 32)
+    scale = (x.abs().amax(dim=-1) / 127.0).to(torch.float16)
+    s32 = scale.float().unsqueeze(-1)
+    q = torch.where(s32 > 0, x / torch.where(s32 > 0, s32, torch.ones_like(s32)), torch.zeros_like(x))
+    codes = (torch.sign(q) * torch.floor(q.abs() + 0.5)).clamp(-127, 127).to(torch.int8)
+    return codes.reshape(S, n, 1, D).contiguous(), scale.contiguous()

@@ -240,3 +240,24 @@ def test_index_share_rule_matches_the_oracle():
     L = dsa.lib()
     assert L.dsa_index_share_source(-1) == PARAM
     assert [L.dsa_index_share_source(il) for il in range(200)] == [O.index_share_source(il) for il in range(200)]
+
+
+@no_gpu
+def test_q8_latent_attention_rejects():
+    # q8_0 latent rows: the MLA shapes only, with a Q of bf16 and the scales given
+    L = dsa.lib()
+
+    def attn(**kw):
+        d = AttnDesc(FAKE, FAKE, FAKE, 576 * 100, 576, 576, 576 * 100, 576, 576, FAKE, None, 1, 0,
+                     1, 1, 128, 1, 576, 512, 100, 64, 1, 0.0, 4, FAKE)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return L.dsa_sparse_attn(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, 0, None)
+
+    assert attn(kv_scale=None) == NULL
+    assert attn(dtype=0) == DTYPE                 # Q must be bf16
+    assert attn(kv_format=7) == DTYPE
+    assert attn(Dk=128, Dv=128) == UNSUP          # q8_0 rows are MLA latents only
+    assert attn(Hkv=2, Hq=128) == UNSUP
+    assert attn(kv_scale=FAKE + 4) == ALIGN
+    assert attn(k_tok_stride=584, v_tok_stride=584) == ALIGN   # byte rows on 16-byte boundaries
