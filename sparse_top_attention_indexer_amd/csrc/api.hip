@@ -353,6 +353,7 @@ struct ForwardPlan {
   int32_t k_out;
   size_t off_pooled, off_scores, off_idx, off_topk, off_attn, total;
   bool multiblock;
+  bool attn_dense;   // top_k >= n_kv: every query selects all its visible keys
   AttnParams ap;
 };
 
@@ -452,7 +453,12 @@ int plan_forward(const dsa_forward_desc* d, ForwardPlan* f) {
   f->off_topk = off;
   if (n_units > 0) off += a256(topk_workspace_bytes(rows, n_units));
   f->off_attn = off;
-  f->ap = attn_params(&ad, reinterpret_cast<const int32_t*>(16), d->out);   // idx bound later
+  // With top_k >= n_kv the selection is every visible key (in block mode
+  // every complete block and the tail), so attention runs as dense causal
+  // attention: the same token set, and the result of the dense call bit for
+  // bit (ik_llama.cpp PR #2058, first commit: the indexer is an exact no-op).
+  f->attn_dense = d->top_k >= d->n_kv;
+  f->ap = attn_params(&ad, f->attn_dense ? nullptr : reinterpret_cast<const int32_t*>(16), d->out);   // idx bound later
   off += a256(attn_workspace_bytes(f->ap));
   f->total = off;
   return DSA_OK;
@@ -533,7 +539,7 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
   }
   DSA_TRY(mark(2));
   AttnParams ap = f.ap;
-  ap.idx = idx;
+  ap.idx = f.attn_dense ? nullptr : idx;
   ap.part = reinterpret_cast<float*>(ws + f.off_attn);
   DSA_TRY(launch_attention(ap, s, ev ? static_cast<hipEvent_t>(ev[3]) : nullptr));
   DSA_TRY(mark(4));

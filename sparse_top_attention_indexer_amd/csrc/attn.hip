@@ -1229,6 +1229,429 @@ __global__ __launch_bounds__(64, 2) void attn_gqa_kernel(AttnParams p) {
   }
 }
 
+// ===================================================== GQA query tiles ==
+
+// Workgroup of the query-tile kernel: GT_WAVES waves, each with two groups
+// of 16 MFMA columns; a column is a (query, head) pair of one KV group, so a
+// workgroup takes 128 / G consecutive queries of one sequence (G = heads per
+// group, a divisor of 16).
+constexpr int GT_WAVES = 8;
+constexpr int GT_CG = 1;                     // 16-column groups per wave
+constexpr int GT_NL = 8 / GT_WAVES;          // 1 KB K (and V) loads per wave and tile
+constexpr int GT_KV = TILE * GQA_D * 2;      // K (or V) rows of one tile of one group (8 KB)
+constexpr int GT_BUF = 2 * GT_KV;            // one tile: K rows, then V rows
+constexpr int GT_NBUF = 4;                   // a pair computed, a pair being loaded
+constexpr int GT_QMAX = GT_WAVES * GT_CG * 16;   // queries of a workgroup (G = 1)
+constexpr int GT_MAX_TILES = 2048;           // key tiles of one split
+constexpr int GT_MAX_CNT = 16384;            // (query, block) multiplicities in LDS (u16)
+
+static int gt_queries(const AttnParams& p) { return GT_WAVES * GT_CG * 16 / (p.Hq / p.Hkv); }
+static int64_t gt_blocks(const AttnParams& p) { return p.idx ? p.n_kv / p.c : 0; }
+
+// The query-tile kernel takes GQA calls in dense mode and in block mode with
+// blocks of a multiple of 32 tokens, when a sequence has enough queries to
+// share the K/V tiles (decode rows stay on attn_gqa_kernel's gather).
+bool gqa_tiled(const AttnParams& p) {
+  if (p.family != ATTN_GQA) return false;
+  const int G = p.Hq / p.Hkv;
+  if (16 % G || p.n_q < 8) return false;
+  if (p.idx && (p.c == 1 || p.c % TILE)) return false;
+  if (gt_queries(p) * gt_blocks(p) > GT_MAX_CNT) return false;
+  const int64_t lim = int64_t(1) << 32;   // 32-bit row offsets within a sequence
+  return p.n_kv * p.k_tok * 2 < lim && p.n_kv * p.v_tok * 2 < lim;
+}
+
+static size_t gt_lds_bytes(const AttnParams& p) {
+  const size_t cnt = (static_cast<size_t>(gt_queries(p)) * gt_blocks(p) + 1) / 2 * 4;
+  return GT_NBUF * GT_BUF + 64 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + cnt;
+}
+static constexpr size_t GT_LDS_MAX = GT_NBUF * GT_BUF + 64 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + GT_MAX_CNT * 2;
+
+// Workgroups: (sequence, split, query tile) units times the KV groups; as in
+// gqa_grid, workgroup b runs on XCD b % 8 and takes its group from b % 8
+// when the group count divides 8, so that the workgroups of one XCD stream
+// the K/V tiles of one group, in the same order, through its L2.
+static int64_t gt_grid(const AttnParams& p) {
+  const int64_t n_qt = (p.n_q + gt_queries(p) - 1) / gt_queries(p);
+  const int64_t n = static_cast<int64_t>(p.S) * p.n_split * n_qt * p.Hkv;
+  return 8 % p.Hkv == 0 ? (n + 7) / 8 * 8 : n;
+}
+
+// One workgroup = a tile of consecutive queries of one sequence x one KV group
+// g x one split of the key positions.  Attention over a query's selected
+// tokens is attention over all positions with the others weighted zero: the
+// workgroup walks the key positions of its split in tiles of 32, skipping
+// tiles that no query of the tile attends to, and each tile's K and V rows
+// go once into LDS (direct global -> LDS loads, two tiles ahead), where all
+// 128 columns read them.  A query's weight for a token is its multiplicity:
+// in block mode the number of times its idx row lists the token's block
+// (live entries: 0 <= b < n_cb), and 1 for the incomplete tail n_cb c ..
+// n_vis - 1; in dense mode 1 for every visible token.  A list that names a
+// block twice thus counts its tokens twice, as the list semantics of the
+// gathered stream do; the summation runs in position order instead of list
+// order.  A tile lies in one block (32 | c), so its multiplicity per query
+// is one count, read from an LDS table built from the idx rows.
+//   scores  S^T (32 keys x 16 columns) = K_tile . Q^T, 16x16x32 MFMAs, K
+//           fragments read once per tile for both column groups
+//   softmax per column (attn_mla_kernel's lazy running max and bf16
+//           weights plus residual), masked entries -inf
+//   PV      O^T (128 dims x 16 columns) += V^T . P^T, V^T fragments through
+//           the transposing LDS read, once per tile for both groups
+// A column group whose queries all skip a tile skips its products.
+// K row t keeps 16-byte chunk c of its 256 bytes in slot c ^ (t & 15) and
+// V row t its 32-byte dim block b in slot b ^ (t & 7) (attn_gqa_kernel's V
+// layout): the fragment reads are free of bank conflicts.
+__global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnParams p) {
+  constexpr int NT = 64 * GT_WAVES;
+  extern __shared__ __align__(16) uint8_t s_raw[];
+  uint8_t* s_kv = s_raw;                                                          // GT_NBUF tiles
+  uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_raw + GT_NBUF * GT_BUF);      // 16 words
+  int32_t* s_nv = reinterpret_cast<int32_t*>(s_scr + 16);                        // n_vis per query
+  int32_t* s_tl = s_nv + GT_QMAX;                                                // first tail token per query
+  uint16_t* s_tiles = reinterpret_cast<uint16_t*>(s_tl + GT_QMAX);               // needed tiles of the split
+  uint32_t* s_cnt = reinterpret_cast<uint32_t*>(s_tiles + GT_MAX_TILES);         // multiplicities, u16 pairs
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.Hq / p.Hkv, QPC = 16 / G, QT = GT_WAVES * GT_CG * QPC;
+  const int64_t n_qt = (p.n_q + QT - 1) / QT;
+  const int64_t b = blockIdx.x;
+  int64_t unit;
+  int g;
+  if (8 % p.Hkv == 0) {
+    g = static_cast<int>((b & 7) % p.Hkv);
+    unit = (b >> 3) * (8 / p.Hkv) + (b & 7) / p.Hkv;
+  } else {
+    g = static_cast<int>(b % p.Hkv);
+    unit = b / p.Hkv;
+  }
+  if (unit >= static_cast<int64_t>(p.S) * p.n_split * n_qt) return;   // padding of the last group of 8
+  const int qt = static_cast<int>(unit % n_qt);
+  const int sp = static_cast<int>((unit / n_qt) % p.n_split);
+  const int s = static_cast<int>(unit / n_qt / p.n_split);
+  const int64_t row0 = static_cast<int64_t>(s) * p.n_q + static_cast<int64_t>(qt) * QT;
+  const int nqt = min(QT, static_cast<int>(p.n_q - static_cast<int64_t>(qt) * QT));   // real queries
+  const bool blk = p.idx != nullptr;
+  const int nb = blk ? static_cast<int>(p.n_kv / p.c) : 0;
+  const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_kv;
+
+  // per query: visible tokens and the first tail token (dense: 0)
+  if (tid < GT_QMAX) {
+    int32_t nv = 0, tl = 0;
+    if (tid < nqt) {
+      nv = static_cast<int32_t>(visible_tokens(p.q_pos[row0 + tid], kl, p.n_kv));
+      tl = blk ? nv / p.c * p.c : 0;
+    }
+    s_nv[tid] = nv;
+    s_tl[tid] = tl;
+  }
+  const int cnt_words = (QT * nb + 1) / 2;
+  for (int i = tid; i < cnt_words; i += NT) s_cnt[i] = 0u;
+  __syncthreads();
+  auto count = [&](int qi, int bl) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t at = static_cast<uint32_t>(qi * nb + bl);
+    return (s_cnt[at >> 1] >> (16 * (at & 1))) & 0xffffu;
+  };
+  if (blk) {
+    const int ne = nqt * p.k_sel;
+    for (int e = tid; e < ne; e += NT) {
+      const int qi = e / p.k_sel;
+      const int32_t bl = p.idx[(row0 + qi) * p.k_sel + (e - qi * p.k_sel)];
+      if (bl >= 0 && bl < s_tl[qi] / p.c) {
+        const uint32_t at = static_cast<uint32_t>(qi * nb + bl);
+        atomicAdd(&s_cnt[at >> 1], 1u << (16 * (at & 1)));
+      }
+    }
+  }
+  int32_t vmax = 0;
+  for (int i = 0; i < nqt; ++i) vmax = max(vmax, s_nv[i]);
+  __syncthreads();   // the multiplicities
+
+  // the split's key tiles that some query attends to, in position order
+  const int64_t k0 = static_cast<int64_t>(sp) * p.split_len;
+  const int64_t k1 = min(k0 + p.split_len, static_cast<int64_t>(vmax));
+  const int kt0 = static_cast<int>(k0 / TILE);
+  const int ntl = k1 > k0 ? static_cast<int>((k1 - k0 + TILE - 1) / TILE) : 0;
+  auto needed = [&](int kt) __attribute__((always_inline)) -> bool {
+    const int t0 = kt * TILE;
+    const int bl = blk ? t0 / p.c : 0;
+    for (int qi = 0; qi < nqt; ++qi) {
+      if (t0 >= s_nv[qi]) continue;
+      if (t0 >= s_tl[qi] || count(qi, bl) != 0u) return true;
+    }
+    return false;
+  };
+  {
+    const int per = (ntl + NT - 1) / NT;
+    const int e0 = min(tid * per, ntl), e1 = min(e0 + per, ntl);
+    uint32_t n = 0;
+    for (int e = e0; e < e1; ++e) n += needed(kt0 + e);
+    uint32_t tot;
+    uint32_t w = block_excl_scan<GT_WAVES>(n, s_scr, &tot);
+    for (int e = e0; e < e1; ++e)
+      if (needed(kt0 + e)) s_tiles[w++] = static_cast<uint16_t>(e);
+    if (tid == 0) s_scr[8] = tot;
+  }
+  __syncthreads();
+  const int n_need = static_cast<int>(s_scr[8]);
+
+  // columns: group cg of wave wid holds queries (GT_CG wid + cg) QPC .. of the
+  // tile, G heads each; lane (col, q) holds column col
+  const int col = lane & 15, q = lane >> 4;
+  u32x4_t qf[GT_CG][4];
+  int32_t c_qi[GT_CG], c_nv[GT_CG], c_tl[GT_CG];
+  bool c_ok[GT_CG];
+  const int head = g * G + col % G;
+#pragma unroll
+  for (int cg = 0; cg < GT_CG; ++cg) {
+    const int qi = (wid * GT_CG + cg) * QPC + col / G;
+    c_qi[cg] = qi;
+    c_ok[cg] = qi < nqt;
+    c_nv[cg] = s_nv[qi];
+    c_tl[cg] = s_tl[qi];
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((row0 + (c_ok[cg] ? qi : 0)) * p.Hq + head) * GQA_D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[cg][ks] = c_ok[cg] ? *reinterpret_cast<const u32x4_t*>(qr + 32 * ks + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // tile loads: wave w, load i copies tile rows 4 (2 w + i) .. + 3 (1 KB of
+  // K, then of V); lane L fills slot L % 16 of row 4 (2 w + i) + L / 16.
+  // Rows no query of the tile sees read row 0 (zero weight).
+  const uint32_t kv_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_kv));
+  const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) + s * p.k_seq + g * p.k_head);
+  const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + s * p.v_seq + g * p.v_head);
+  const uint32_t kpitch = static_cast<uint32_t>(p.k_tok) * 2u, vpitch = static_cast<uint32_t>(p.v_tok) * 2u;
+  // lane offsets within a tile (rows r = 4 (2 w + i) + lane / 16) and the
+  // same rows' offsets for row 0 (rows past every query's view)
+  uint32_t k_lo[GT_NL], v_lo[GT_NL], k_r0[GT_NL], v_r0[GT_NL];
+#pragma unroll
+  for (int i = 0; i < GT_NL; ++i) {
+    const uint32_t r = 4 * (GT_NL * wid + i) + (lane >> 4), sl = lane & 15;
+    k_r0[i] = 16u * (sl ^ (r & 15));
+    v_r0[i] = 16u * ((2u * ((sl >> 1) ^ (r & 7))) | (sl & 1u));
+    k_lo[i] = r * kpitch + k_r0[i];
+    v_lo[i] = r * vpitch + v_r0[i];
+  }
+  auto load_tile = [&](int kt, int bf) __attribute__((always_inline)) {
+    const int t0 = kt * TILE;
+    const bool whole = t0 + TILE <= vmax;   // wave-uniform
+    const uint32_t kb0 = static_cast<uint32_t>(t0) * kpitch, vb0 = static_cast<uint32_t>(t0) * vpitch;
+#pragma unroll
+    for (int i = 0; i < GT_NL; ++i) {
+      uint32_t ko = kb0 + k_lo[i], vo = vb0 + v_lo[i];
+      if (!whole) {
+        const bool in = t0 + 4 * (GT_NL * wid + i) + (lane >> 4) < vmax;
+        ko = in ? ko : k_r0[i];
+        vo = in ? vo : v_r0[i];
+      }
+      const uint32_t lb = kv_lds + static_cast<uint32_t>(bf * GT_BUF) + 1024u * (GT_NL * wid + i);
+      dma16(kb, ko, __builtin_amdgcn_readfirstlane(lb));
+      dma16(vb, vo, __builtin_amdgcn_readfirstlane(lb + GT_KV));
+    }
+  };
+
+  // o[cg][db], db < 8: dims 16 db + 4 q + j of column col (O^T); o[cg][8]:
+  // the column's normaliser in every register, as the product of the
+  // weights with a block of ones, so that it sums exactly the bf16 weights
+  // the value products take
+  f32x4_t o[GT_CG][9];
+#pragma unroll
+  for (int cg = 0; cg < GT_CG; ++cg)
+#pragma unroll
+    for (int db = 0; db < 9; ++db) o[cg][db] = f32x4_t{};
+  float m_run[GT_CG];
+#pragma unroll
+  for (int cg = 0; cg < GT_CG; ++cg) m_run[cg] = NEG_INF;
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+  const float c2 = p.scale_log2;
+  const uint32_t vr_m = (lane >> 2) & 3, vr_r = lane & 3, vr_R = 4 * q + vr_m;
+
+  // O^T += V^T . P^T for the column groups in `cgs` (a pack of 0 / 1 flags)
+  // with weights pw, straight-line: V^T fragments read two ahead, once per
+  // tile for every group (attn_gqa_kernel's addressing)
+  auto pv = [&](auto cgs, int bf, const u32x4_t (&pw)[GT_CG]) __attribute__((always_inline)) {
+    constexpr int W0 = decltype(cgs)::value & 1, W1 = decltype(cgs)::value >> 1;
+    const uint8_t* vt_ = s_kv + bf * GT_BUF + GT_KV;
+    auto vfrag = [&](int db) __attribute__((always_inline)) -> u32x4_t {
+      const uint8_t* a2 = vt_ + vr_R * 256 + 32 * (db ^ (vr_R & 7)) + 8 * vr_r;
+      const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a2);
+      const v4i16_t vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a2 + 16 * 256));
+      const u32x2_t u2 = __builtin_bit_cast(u32x2_t, va), w2 = __builtin_bit_cast(u32x2_t, vc);
+      return u32x4_t{u2.x, u2.y, w2.x, w2.y};
+    };
+    constexpr int VD = 2;
+    u32x4_t vf[VD];
+#pragma unroll
+    for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
+    if constexpr (W0 != 0) o[0][8] = mfma16x16x32_bf16(ones, pw[0], o[0][8]);
+    if constexpr (W1 != 0 && GT_CG > 1) o[GT_CG - 1][8] = mfma16x16x32_bf16(ones, pw[GT_CG - 1], o[GT_CG - 1][8]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if constexpr (W0 != 0) o[0][db] = mfma16x16x32_bf16(vf[db % VD], pw[0], o[0][db]);
+      if constexpr (W1 != 0 && GT_CG > 1) o[GT_CG - 1][db] = mfma16x16x32_bf16(vf[db % VD], pw[GT_CG - 1], o[GT_CG - 1][db]);
+      if (db + VD < 8) vf[db % VD] = vfrag(db + VD);
+    }
+  };
+  using both_t = std::integral_constant<int, 3>;
+  using first_t = std::integral_constant<int, 1>;
+  using second_t = std::integral_constant<int, 2>;
+
+  // the multiplicity table's row of each column's query
+  int32_t c_cb[GT_CG];
+#pragma unroll
+  for (int cg = 0; cg < GT_CG; ++cg) c_cb[cg] = c_qi[cg] * nb;
+  auto compute = [&](int bf, int kt, int bl) __attribute__((always_inline)) {
+    const int t0 = kt * TILE;
+    const int blc = bl < nb ? bl : nb - 1;   // a tile past the complete blocks is every query's tail
+    uint32_t mult[GT_CG];
+    bool act[GT_CG];
+#pragma unroll
+    for (int cg = 0; cg < GT_CG; ++cg) {
+      uint32_t cnt = 1u;
+      if (nb > 0) {
+        const uint32_t at = static_cast<uint32_t>(c_cb[cg] + blc);
+        cnt = (s_cnt[at >> 1] >> (16 * (at & 1))) & 0xffffu;
+      }
+      const bool vis = c_ok[cg] && t0 < c_nv[cg];
+      mult[cg] = vis ? (t0 >= c_tl[cg] ? 1u : cnt) : 0u;
+      act[cg] = __ballot(mult[cg] != 0u) != 0;
+    }
+    bool any = false;
+#pragma unroll
+    for (int cg = 0; cg < GT_CG; ++cg) any = any || act[cg];
+    if (!any) return;
+    const uint8_t* kt_ = s_kv + bf * GT_BUF;
+    // K fragment (mb, ks): tile row 16 mb + col, chunk 4 ks + q
+    u32x4_t kf[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[mb][ks] = *reinterpret_cast<const u32x4_t*>(kt_ + (16 * mb + col) * 256 + 16 * ((4 * ks + q) ^ col));
+    u32x4_t ph[GT_CG], pl[GT_CG];
+    bool lo[GT_CG];
+#pragma unroll
+    for (int cg = 0; cg < GT_CG; ++cg) {
+      lo[cg] = false;
+      ph[cg] = pl[cg] = u32x4_t{0u, 0u, 0u, 0u};
+      if (!act[cg]) continue;
+      f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s0 = mfma16x16x32_bf16(kf[0][ks], qf[cg][ks], s0);
+        s1 = mfma16x16x32_bf16(kf[1][ks], qf[cg][ks], s1);
+      }
+      // reg j of s_mb: key t0 + 16 mb + 4 q + j of column col.  A column whose
+      // query skips the tile (mult 0) keeps its scores out of the max and
+      // gets zero weights through an infinite offset; keys past a query's
+      // last visible token (only in a tile that crosses it) are -inf.
+      const int lim = c_nv[cg] - t0 - 4 * q;   // keys j < lim (+ 16 mb) are visible
+      if (__ballot(mult[cg] != 0u && t0 + TILE > c_nv[cg]) != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j >= lim) s0[j] = NEG_INF;
+          if (16 + j >= lim) s1[j] = NEG_INF;
+        }
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      tmax = quad_max(tmax);
+      tmax = mult[cg] != 0u ? tmax : NEG_INF;
+      const bool first = m_run[cg] == NEG_INF;
+      const bool grow = !first && (tmax - m_run[cg]) * c2 > 8.f;
+      const float a = __builtin_amdgcn_exp2f((m_run[cg] - tmax) * c2);
+      const float alpha = grow ? a : 1.f;
+      m_run[cg] = (first || grow) ? tmax : m_run[cg];
+      float mb_ = m_run[cg] == NEG_INF ? 0.f : m_run[cg] * c2;
+      // the multiplicity scales the weights: offset log2(mult), zero -> +inf
+      if (__ballot(mult[cg] > 1u) != 0) mb_ -= __builtin_amdgcn_logf(static_cast<float>(mult[cg] > 1u ? mult[cg] : 1u));
+      mb_ = mult[cg] != 0u ? mb_ : __builtin_inff();
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -mb_));
+        x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb_));
+      }
+      uint32_t hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      ph[cg] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+      // the tile adds at least its largest weight to the rescaled normaliser
+      const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb_));
+      lo[cg] = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[cg][8][0] * alpha) != 0;
+      if (lo[cg]) {
+        uint32_t lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
+        pl[cg] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+      }
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int db = 0; db < 9; ++db) o[cg][db] *= alpha;
+      }
+    }
+    if constexpr (GT_CG == 2) {
+      if (act[0] && act[1]) pv(both_t{}, bf, ph);
+      else if (act[0]) pv(first_t{}, bf, ph);
+      else pv(second_t{}, bf, ph);
+      if (lo[0] && lo[1]) pv(both_t{}, bf, pl);
+      else if (lo[0]) pv(first_t{}, bf, pl);
+      else if (lo[1]) pv(second_t{}, bf, pl);
+    } else {
+      pv(first_t{}, bf, ph);
+      if (lo[0]) pv(first_t{}, bf, pl);
+    }
+  };
+
+  // pipeline over pairs of tiles: the loads of pair u + 2, u + 3 run while
+  // pair u, u + 1 is computed; the barrier before them (into the buffers of
+  // pair u - 2) also ends every wave's reads of those buffers.  Tile and
+  // block ids are wave-uniform (scalar registers).
+  const int tpb = blk ? p.c / TILE : 1;   // tiles per block
+  auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
+    return kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s_tiles[u])));
+  };
+  if (n_need > 0) load_tile(tile_at(0), 0);
+  if (n_need > 1) load_tile(tile_at(1), 1);
+  for (int u = 0; u < n_need; u += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this pair's loads have landed
+    __syncthreads();
+    if (u + 2 < n_need) load_tile(tile_at(u + 2), (u + 2) % GT_NBUF);
+    if (u + 3 < n_need) load_tile(tile_at(u + 3), (u + 3) % GT_NBUF);
+    const int ka = tile_at(u);
+    compute(u % GT_NBUF, ka, ka / tpb);
+    if (u + 1 < n_need) {
+      const int kb_ = tile_at(u + 1);
+      compute((u + 1) % GT_NBUF, kb_, kb_ / tpb);
+    }
+  }
+
+  // output: accumulator (cg, db, j) holds dim 16 db + 4 q + j of column col
+#pragma unroll
+  for (int cg = 0; cg < GT_CG; ++cg) {
+    if (!c_ok[cg]) continue;
+    const int64_t row = row0 + c_qi[cg];
+    if (p.n_split == 1) {
+      const float inv = o[cg][8][0] > 0.f ? 1.f / o[cg][8][0] : 0.f;
+      const int64_t ob = (row * p.Hq + head) * GQA_D + 4 * q;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        store4(p.out, p.o_dtype, ob + 16 * db, o[cg][db][0] * inv, o[cg][db][1] * inv, o[cg][db][2] * inv,
+               o[cg][db][3] * inv);
+    } else {
+      float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(GQA_D);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[cg][db];
+      if (q == 0) {
+        pp[GQA_D] = m_run[cg];
+        pp[GQA_D + 1] = o[cg][8][0];
+      }
+    }
+  }
+}
+
 // ============================================================== f32 kernel ==
 
 constexpr size_t F32_LDS = 64 * 4 * 2 + 64 + MAX_BLOCKS * 4;
@@ -1399,6 +1822,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // ================================================================== host ==
 
 void attn_plan(AttnParams& p, int64_t list_len) {
+  if (gqa_tiled(p)) {
+    // splits of the key positions: two workgroups per CU, at least 16 tiles
+    // and at most GT_MAX_TILES tiles a split
+    const int64_t wgs = static_cast<int64_t>(p.S) * ((p.n_q + gt_queries(p) - 1) / gt_queries(p)) * p.Hkv;
+    int64_t ns = wgs < 512 ? (512 + wgs - 1) / wgs : 1;
+    const int64_t max_ns = (p.n_kv + 16 * TILE - 1) / (16 * TILE);
+    if (ns > max_ns) ns = max_ns;
+    const int64_t min_ns = (p.n_kv + int64_t(GT_MAX_TILES) * TILE - 1) / (int64_t(GT_MAX_TILES) * TILE);
+    if (ns < min_ns) ns = min_ns;
+    int64_t sl = (p.n_kv + ns - 1) / ns;
+    sl = (sl + TILE - 1) / TILE * TILE;
+    p.n_split = static_cast<int32_t>((p.n_kv + sl - 1) / sl);
+    p.split_len = static_cast<int32_t>(sl);
+    return;
+  }
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   int64_t wgs;   // workgroups per split
   int64_t target;
@@ -1451,6 +1889,13 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_mla_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hq + 127) / 128),
                        dim3(64 * MLA_WAVES), MLA_LDS, st, p);
+  } else if (gqa_tiled(p)) {
+    // the largest size any call uses, so that concurrent calls set the same value
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_tile_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GT_LDS_MAX));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_gqa_tile_kernel, dim3(static_cast<unsigned>(gt_grid(p))), dim3(64 * GT_WAVES),
+                       gt_lds_bytes(p), st, p);
   } else if (p.family == ATTN_GQA) {
     // the largest size any call uses, so that concurrent calls set the same value
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_kernel),
