@@ -85,6 +85,16 @@ def score_kernel_name(wl):
     return "score_mfma_kernel"
 
 
+def attn_kernel_name(wl):
+    """The attention kernel the library picks for workload wl: GQA calls with
+    8+ queries a sequence in dense mode or with blocks of a multiple of 32
+    tokens run over query tiles."""
+    if wl.attn == "gqa":
+        tiled = wl.n_q >= 8 and (wl.c > 1 and wl.c % 32 == 0) and 16 % (wl.Hq // wl.Hkv) == 0
+        return "attn_gqa_tile_kernel" if tiled else "attn_gqa_kernel"
+    return {"mla": "attn_mla_kernel", "f32": "attn_f32_kernel"}[wl.attn]
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE record (calibrated by a copy of known
@@ -476,8 +486,7 @@ def time_workload(dsa, inputs, torch, wl, steps, warmup, flush):
     else:
         roof = {"bound": "hbm", "achieved": ph["bytes"] / t_dom / 1e9, "peak": ph["peak"] / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = {"scores": score_kernel_name(wl), "topk": "topk kernels", "attn":
-                      {"mla": "attn_mla_kernel", "gqa": "attn_gqa_kernel", "f32": "attn_f32_kernel"}[wl.attn]}[dom]
+    roof["kernel"] = {"scores": score_kernel_name(wl), "topk": "topk kernels", "attn": attn_kernel_name(wl)}[dom]
     roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["launch_ms"] = launch_ms[dom]
     step_bytes = sum(work[n_]["bytes"] for n_ in ("scores", "topk", "attn"))
@@ -511,6 +520,15 @@ def time_workload(dsa, inputs, torch, wl, steps, warmup, flush):
     return res, x
 
 
+def calib_copy(torch):
+    """One 1 GiB device-to-device copy: known bytes (1048576 KiB read and
+    written) that calibrate the FETCH_SIZE / WRITE_SIZE counters of a run."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -528,6 +546,8 @@ def main():
                                         "index_share": index_share_row(dsa, inputs, torch, 5),
                                         "q8_0_latent": q8_latent_row(dsa, inputs, torch, 10, flush)}}),
               flush=True)
+        if args.calib_copy:
+            calib_copy(torch)
         return
     headline = args.config if args.config is not None else 2
     # Before each timed step a 1 GiB read evicts the L2s and the 256 MB
@@ -576,10 +596,7 @@ def main():
                              "index_share": index_share_row(dsa, inputs, torch, 5),
                              "q8_0_latent": q8_latent_row(dsa, inputs, torch, 10, flush)}
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+        calib_copy(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
         if headline in (1, 3):   # the small and the batched-decode workloads also on one core
