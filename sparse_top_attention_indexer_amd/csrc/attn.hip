@@ -296,10 +296,14 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   }
   const int n_tiles = p1 > p0 ? static_cast<int>((p1 - p0 + TILE - 1) / TILE) : 0;
 
-  f32x4_t o[32];
+  // o[db]: O^T dims 16 db + 4 q + j of head `head`; o[32]: the head's
+  // normaliser in every register, the product of the weights with a block of
+  // ones, so that it sums exactly the bf16 weights the value products take
+  f32x4_t o[33];
 #pragma unroll
-  for (int db = 0; db < 32; ++db) o[db] = f32x4_t{};
-  float m_run = NEG_INF, l_run = 0.f;
+  for (int db = 0; db < 33; ++db) o[db] = f32x4_t{};
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+  float m_run = NEG_INF;
   const float c2 = p.scale_log2;
 
   const uint32_t kb_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_kb));
@@ -419,28 +423,28 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       x[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -mb));
       x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb));
     }
-    uint32_t hv[4], lv[4];
-    float psum = 0.f, hsum = 0.f;
+    uint32_t hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-      const float h0 = __uint_as_float(hv[i] << 16), h1 = __uint_as_float(hv[i] & 0xffff0000u);
-      lv[i] = pack_bf16x2(x[2 * i] - h0, x[2 * i + 1] - h1);
-      psum += x[2 * i] + x[2 * i + 1];
-      hsum += h0 + h1;
-    }
+    for (int i = 0; i < 4; ++i) hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     ph = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-    pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
-    const float la = l_run * alpha, l_full = la + quad_sum(psum);
+    // the residual pass when the head's largest weight in the tile is large
+    // against its normaliser: the tile adds at least that weight to the
+    // rescaled normaliser so far
     const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));   // the head's largest weight in the tile
-    need_lo = __ballot(xmax > LO_SHARE * l_full) != 0;   // wave-uniform
-    l_run = need_lo ? l_full : la + quad_sum(hsum);
+    need_lo = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[32][0] * alpha) != 0;   // wave-uniform
+    if (need_lo) {
+      uint32_t lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
+      pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+    }
     return alpha;
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
-    if (alpha != 1.f) {
+    if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int db = 0; db < 32; ++db) o[db] *= alpha;
+      for (int db = 0; db < 33; ++db) o[db] *= alpha;
     }
   };
   // V^T fragment of dim block db: lane (q, source slot 4 m + r) addresses key
@@ -471,6 +475,7 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
 #pragma unroll
     for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * VD, 0);
+    o[32] = mfma16x16x32_bf16(ones, pw, o[32]);
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
       o[db] = mfma16x16x32_bf16(vf[db % VD], pw, o[db]);
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   auto write_out = [&]() __attribute__((always_inline)) {
     if (!(wvalid && head < p.Hq)) return;
     if (p.n_split == 1) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      const float inv = o[32][0] > 0.f ? 1.f / o[32][0] : 0.f;
       const int64_t ob = (row * p.Hq + head) * MLA_DV + 4 * q;
 #pragma unroll
       for (int db = 0; db < 32; ++db)
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
         *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
       if (q == 0) {
         pp[MLA_DV] = m_run;
-        pp[MLA_DV + 1] = l_run;
+        pp[MLA_DV + 1] = o[32][0];
       }
     }
   };
