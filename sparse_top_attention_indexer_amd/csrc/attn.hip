@@ -1526,6 +1526,7 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
 #pragma unroll
     for (int cg = 0; cg < GT_CG; ++cg) any = any || act[cg];
     if (!any) return;
+    __builtin_amdgcn_s_setprio(2);   // the score chain and softmax first; other waves' products fill the gaps
     const uint8_t* kt_ = s_kv + bf * GT_BUF;
     // K fragment (mb, ks): tile row 16 mb + col, chunk 4 ks + q
     u32x4_t kf[2][4];
@@ -1597,6 +1598,7 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
         for (int db = 0; db < 9; ++db) o[cg][db] *= alpha;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (GT_CG == 2) {
       if (act[0] && act[1]) pv(both_t{}, bf, ph);
       else if (act[0]) pv(first_t{}, bf, ph);
