@@ -191,11 +191,12 @@ __device__ __forceinline__ float quad_sum(float x) {
 //   O^T (512 dims x 16 heads) += V^T . P^T: V^T fragments come straight from
 //       the key-major tile through the transposing LDS read; P^T is the S^T
 //       accumulator layout, so no data moves between lanes
-// Work runs in segments separated by barriers: a wave computes the scores and
-// softmax of tile u in one segment and its PV products in the next, and
-// waves 4..7 run one segment behind waves 0..3, so on every SIMD (waves w and
-// w + 4) one wave's score products and exponentials overlap the other wave's
-// PV products.  Tiles are gathered with direct global -> LDS loads two
+// Work runs in segments separated by barriers: a wave computes the scores of
+// tile u, their running max and the residual decision in one segment, and
+// the exponentials, the bf16 weights and the PV products in the next; waves
+// 4..7 run one segment behind waves 0..3, so on every SIMD (waves w and w + 4)
+// one wave's score products overlap the other wave's exponentials and PV
+// products.  Tiles are gathered with direct global -> LDS loads two
 // segments ahead (three tile buffers).  Token ids of the stream sit in an LDS
 // ring of 32 tiles, refilled 16 tiles ahead.
 __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams p) {
@@ -399,8 +400,11 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
   // P^T fragments (k slot j < 4: key 4 q + j; j >= 4: key 16 + 4 q + j - 4)
   // and returns the factor that rescales what was accumulated before.
-  auto softmax = [&](f32x4_t s0, f32x4_t s1, uint32_t live, u32x4_t& ph, u32x4_t& pl,
-                     bool& need_lo) __attribute__((always_inline)) -> float {
+  // online softmax, first half (in the score segment): masks dead entries,
+  // moves the running max, decides the residual pass, and returns the factor
+  // that rescales what was accumulated before; the exponent offset goes to mb
+  auto softmax_a = [&](f32x4_t& s0, f32x4_t& s1, uint32_t live, float& mb, bool& need_lo)
+                       __attribute__((always_inline)) -> float {
     if (live != 0xffffffffu) {
       const uint32_t lm = live >> (4 * q);
 #pragma unroll
@@ -416,7 +420,15 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
     const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
     const float alpha = grow ? a : 1.f;
     m_run = (first || grow) ? tmax : m_run;
-    const float mb = m_run == NEG_INF ? 0.f : m_run * c2;   // an all-dead prefix gives zero weights
+    mb = m_run == NEG_INF ? 0.f : m_run * c2;   // an all-dead prefix gives zero weights
+    const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));   // the head's largest weight in the tile
+    need_lo = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[32][0] * alpha) != 0;   // wave-uniform
+    return alpha;
+  };
+  // second half (in the PV segment): the weights as bf16 high parts, and
+  // their residual when the tile runs the residual pass
+  auto softmax_b = [&](f32x4_t s0, f32x4_t s1, float mb, bool need_lo, u32x4_t& ph, u32x4_t& pl)
+                       __attribute__((always_inline)) {
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -427,11 +439,6 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     ph = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-    // the residual pass when the head's largest weight in the tile is large
-    // against its normaliser: the tile adds at least that weight to the
-    // rescaled normaliser so far
-    const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));   // the head's largest weight in the tile
-    need_lo = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[32][0] * alpha) != 0;   // wave-uniform
     if (need_lo) {
       uint32_t lv[4];
 #pragma unroll
@@ -439,7 +446,6 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
         lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
       pl = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
     }
-    return alpha;
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (__ballot(alpha != 1.f) != 0) {
@@ -578,15 +584,17 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       f32x4_t s0, s1;
       u32x4_t ph, pl;
       bool need_lo;
+      float mb;
       // tile u + 1 past tile 1 (the first two come whole from the prologue;
       // at u = 0 this reloads rows of tile 1 with the same bytes, and past
       // the stream it loads rows nothing reads)
       __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
       scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), (u + 1) % KT_NBUF);
-      rescale(softmax(s0, s1, live_of(u), ph, pl, need_lo));
+      rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u);
       segment_io(2 * u + 1);
+      softmax_b(s0, s1, mb, need_lo, ph, pl);
       u32x4_t pw = ph;
 #pragma clang loop unroll(disable)
       for (int ps = 0; ps < 1 + need_lo; ++ps) {
@@ -611,13 +619,15 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       f32x4_t s0, s1;
       u32x4_t ph, pl;
       bool need_lo;
+      float mb;
       __builtin_amdgcn_s_setprio(2);
       scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, (u + 2) % KT_NBUF);
-      rescale(softmax(s0, s1, live_of(u), ph, pl, need_lo));
+      rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
       __builtin_amdgcn_s_setprio(0);
       segment_end(2 * u + 1);
       segment_io(2 * u + 2);
       g_tl = tokens_of(u + 3);   // for the next score segment
+      softmax_b(s0, s1, mb, need_lo, ph, pl);
       u32x4_t pw = ph;
 #pragma clang loop unroll(disable)
       for (int ps = 0; ps < 1 + need_lo; ++ps) {
