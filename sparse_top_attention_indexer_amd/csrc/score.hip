@@ -315,8 +315,9 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 // Prefill variant (n_q a multiple of 4, no histogram): one workgroup = 4
 // consecutive query rows of one sequence (one wave each) x one chunk of
 // 32-key tiles.  The key tiles are gathered once per workgroup into LDS with
-// direct global -> LDS loads, three tiles ahead (four tile buffers), and read
-// by all four waves.  Three workgroups share a CU (148 registers, 48 KB of
+// direct global -> LDS loads in pairs (four tile buffers: one pair is
+// computed while the next lands, one barrier per pair), and read by all four
+// waves.  Three workgroups share a CU (148 registers, 48 KB of
 // LDS), so that three waves per SIMD interleave their products and
 // epilogues; with a rotated or non-bf16 q split into two operands, two
 // workgroups (more registers).  The scores of the chunk
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 // c ^ (r & 15), so that a wave's B-operand read (lane n: row n, chunk
 // 8 h2 + ks) is free of LDS bank conflicts.
 constexpr int SC_TILE_BYTES = 32 * 256;   // one key tile
-constexpr int SC_NBUF = 4;                      // tiles: computing, landed, two in flight
+constexpr int SC_NBUF = 4;                      // tiles: a pair computed, a pair in flight
 constexpr int SC_MAX_TILES = 32;                // chunk_tiles bound for this kernel
 constexpr size_t SC_LDS = SC_NBUF * SC_TILE_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
 
@@ -380,34 +381,42 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   // (two 1 KB loads; lane L of load i: row 8 w + 4 i + L / 16, slot L & 15)
   const uint32_t kt_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((sc_lds_void_t*)s_kt));
   const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * 256;
+  // lane parts of the gather (row r = 8 w + 4 i + lane / 16 of the tile,
+  // swizzled slot) and the tile base; rows past the keys read the last row
+  const uint32_t n_units32 = static_cast<uint32_t>(p.n_units), u_begin32 = static_cast<uint32_t>(u_begin);
+  uint32_t g_r[2], g_sl[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t r = 8 * wid + 4 * i + (lane >> 4);
+    g_r[i] = r;
+    g_sl[i] = 16u * ((lane & 15) ^ (r & 15));
+  }
   auto issue = [&](int T) __attribute__((always_inline)) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    const uint32_t t0 = u_begin32 + 32u * static_cast<uint32_t>(T);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = 8 * wid + 4 * (i & 1) + (ln >> 4);
-      int64_t u = u_begin + static_cast<int64_t>(T) * 32 + r;
-      if (u >= p.n_units) u = p.n_units - 1;   // past the end: any valid row, never used
-      const uint32_t voff = static_cast<uint32_t>(u) * 256u + 16u * ((ln & 15) ^ (r & 15));
-      sc_dma16(kbase, voff,
-               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_TILE_BYTES + 1024u * (2 * wid + (i & 1))));
+      uint32_t u = t0 + g_r[i];
+      u = u < n_units32 ? u : n_units32 - 1;   // past the end: any valid row, never used
+      sc_dma16(kbase, u * 256u + g_sl[i],
+               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_TILE_BYTES + 1024u * (2 * wid + i)));
     }
   };
   if (n_t > 0) issue(0);
   if (n_t > 1) issue(1);
-  if (n_t > 2) issue(2);
 
   u32x4_t qa[RB][8][NQ];
   float wv[RB][16];
   if (n_t > 0) query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
-  const uint32_t b_off = n * 256u;   // + 16 ((8 h2 + ks) ^ (n & 15))
+  // B operand of step ks: row n, chunk 8 h2 + ks in slot (8 h2 + ks) ^ (n & 15)
+  // = ((8 h2) ^ (n & 15)) ^ ks, so the step only flips the low 3 slot bits
+  const uint32_t b_off = n * 256u + 16u * ((8u * h2) ^ (n & 15));
 
-  auto products = [&](const uint8_t* kt, uint32_t hx, f32x16_t (&acc)[RB]) __attribute__((always_inline)) {
+  auto products = [&](uint32_t kof, f32x16_t (&acc)[RB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(kt + 16u * ((hx + ks) ^ (n & 15)));
+      const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(s_kt + (kof ^ (16u * ks)));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if constexpr (F16OP) {
@@ -427,26 +436,30 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
 #pragma unroll
       for (int j = 0; j < 16; ++j) part[j & 3] = fmaf(wv[rb][j], relu(acc[rb][j]), part[j & 3]);
     const float tot = half_sum((part[0] + part[1]) + (part[2] + part[3]));
-    const int64_t u = u_begin + static_cast<int64_t>(t) * 32 + n;
-    if (h2 == 0) s_sc[wid * (SC_MAX_TILES * 32) + t * 32 + n] = u < n_vis ? tot : NEG_INF;
+    const int32_t u = static_cast<int32_t>(u_begin) + t * 32 + n;
+    if (h2 == 0) s_sc[wid * (SC_MAX_TILES * 32) + t * 32 + n] = u < static_cast<int32_t>(n_vis) ? tot : NEG_INF;
   };
 
-  for (int T = 0; T < n_t; ++T) {
-    // tile T has landed: only the loads of tiles T + 1 and T + 2 (two each) may still be in flight
-    if (T + 2 < n_t) __builtin_amdgcn_s_waitcnt(0x0f74);        // vmcnt(4)
-    else if (T + 1 < n_t) __builtin_amdgcn_s_waitcnt(0x0f72);   // vmcnt(2)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
-    __syncthreads();                                             // for every wave; slot of T - 1 free
+  // pairs of tiles: the loads of tiles T + 2, T + 3 run while T, T + 1 are
+  // computed; one barrier per pair (before the loads into the slots of
+  // T - 2, T - 1)
+  for (int T = 0; T < n_t; T += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this pair has landed
+    __syncthreads();
+    if (T + 2 < n_t) issue(T + 2);
     if (T + 3 < n_t) issue(T + 3);
-    if (T < t_own) {
-      const uint8_t* kt = s_kt + (T % SC_NBUF) * SC_TILE_BYTES + b_off;
-      uint32_t hx = 8u * h2;
-      asm volatile("" : "+v"(hx));
-      f32x16_t acc0[RB];
-      __builtin_amdgcn_s_setprio(1);   // the product chain first; the other waves' epilogues fill the gaps
-      products(kt, hx, acc0);
-      __builtin_amdgcn_s_setprio(0);
-      epilogue(acc0, T);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int Tt = T + d;
+      if (Tt < t_own) {
+        uint32_t kof = (Tt % SC_NBUF) * SC_TILE_BYTES + b_off;
+        asm volatile("" : "+v"(kof));
+        f32x16_t acc0[RB];
+        __builtin_amdgcn_s_setprio(1);   // the product chain first; the other waves' epilogues fill the gaps
+        products(kof, acc0);
+        __builtin_amdgcn_s_setprio(0);
+        epilogue(acc0, Tt);
+      }
     }
   }
   // write-out: computed tiles, then -inf for the invisible rest when asked
