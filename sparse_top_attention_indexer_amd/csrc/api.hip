@@ -351,8 +351,10 @@ struct ForwardPlan {
   dsa_attn_desc attn_desc;
   int64_t n_units;
   int32_t k_out;
-  size_t off_pooled, off_scores, off_idx, off_topk, off_attn, total;
+  size_t off_pooled, off_scores, off_idx, off_topk, off_prep, off_attn, total;
   bool multiblock;
+  bool fuse_hist;    // few long rows: the score epilogue builds the top-k histogram
+  bool prep;         // ... in the decode stream kernel, from prepared query operands
   bool attn_dense;   // top_k >= n_kv: every query selects all its visible keys
   AttnParams ap;
 };
@@ -452,6 +454,12 @@ int plan_forward(const dsa_forward_desc* d, ForwardPlan* f) {
   if (!d->idx_out) off += a256(static_cast<size_t>(rows) * f->k_out * 4);
   f->off_topk = off;
   if (n_units > 0) off += a256(topk_workspace_bytes(rows, n_units));
+  // few long rows: the score epilogue builds the top-k histogram ([FIDX])
+  f->fuse_hist = f->multiblock && !topk_use_long(rows, n_units) &&
+                 scores_use_mfma(d->q_idx_dtype, id.k_dtype, d->H, d->D);
+  f->prep = f->fuse_hist && scores_use_prep(d->q_idx_dtype, id.k_dtype, d->H, d->D, n_units);
+  f->off_prep = off;
+  if (f->prep) off += score_prep_bytes(rows, d->q_idx_dtype, id.k_dtype, d->H, d->hadamard_q);
   f->off_attn = off;
   // With top_k >= n_kv the selection is every visible key (in block mode
   // every complete block and the tail), so attention runs as dense causal
@@ -520,14 +528,13 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
       sp.k = pooled;
     }
     TopkParams tp = topk_params(scores, &f.topk_desc, idx);
-    // few long rows: the score epilogue builds the top-k histogram ([FIDX])
-    const bool fuse_hist = f.multiblock && !topk_use_long(rows, f.n_units) &&
-                           scores_use_mfma(sp.q_dtype, sp.k_dtype, sp.H, sp.D);
+    const bool fuse_hist = f.fuse_hist;
     if (f.multiblock) {
       topk_bind_workspace(tp, ws + f.off_topk);
       if (fuse_hist) {
-        DSA_TRY(launch_topk_clear(tp, s));
         sp.hist = tp.hist;
+        if (f.prep) score_prep_bind(sp, ws + f.off_prep);
+        DSA_TRY(launch_score_prep(sp, tp.cand_cnt, s));
       }
     }
     DSA_TRY(launch_scores(sp, s));

@@ -34,11 +34,23 @@ struct ScoreParams {
   int32_t fill_invisible;
   int32_t n_sink;        // hist excludes the forced sinks
   int32_t k_out;         // hist only for rows with more visible units than k_out
+  const uint32_t* qop;   // query operands prepared by score_prep_kernel (decode stream kernel), else null
+  const float* qw;       // their head weights, in the stream kernel's lane layout
 };
 // Chooses a kernel variant and launches it; returns a hipError_t.
 hipError_t launch_scores(ScoreParams p, hipStream_t st);
 // True when the MFMA score kernels cover (q_dtype, k_dtype, H, D).
 bool scores_use_mfma(int q_dtype, int k_dtype, int H, int D);
+// True when rows with the fused top-k histogram take the decode stream
+// kernel, which reads query operands prepared by launch_score_prep.
+bool scores_use_prep(int q_dtype, int k_dtype, int H, int D, int64_t n_units);
+// Bytes of prepared query operands for `rows` rows (256-byte multiple).
+size_t score_prep_bytes(int64_t rows, int q_dtype, int k_dtype, int H, int hadamard);
+// Points p.qop and p.qw into a workspace of score_prep_bytes for p's rows.
+void score_prep_bind(ScoreParams& p, void* ws);
+// Clears the top-k histogram (p.hist) and candidate counts, and when p.qop is
+// set writes the query operands and head weights of every row there.
+hipError_t launch_score_prep(const ScoreParams& p, uint32_t* cand_cnt, hipStream_t st);
 
 // ------------------------------------------------------------------- top-k --
 struct TopkParams {

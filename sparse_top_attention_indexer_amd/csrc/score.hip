@@ -473,6 +473,97 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   }
 }
 
+// Query operands of the decode stream kernel, prepared once per row instead
+// of once per wave (a row's query is shared by every wave that streams its
+// keys).  One wave per (row, head), lane l holding dims 2 l and 2 l + 1; the
+// rotation runs the butterflies of query_operands in the same order (index
+// bit 0 in the lane, bits 1..5 across lanes, bit 6 with the 1/sqrt(128)
+// scale), each output the same f32 sum or difference of the same two values,
+// so the operands are bit for bit those of query_operands.  Outputs, per row
+// r and head block rb (RB = 1 or 2 blocks of 32 heads):
+//   qop: u32x4 [r][rb][ks][nq][64]: the operand qa[rb][ks][nq] of stream lane
+//        n + 32 h2 (head 32 rb + n, dims 64 h2 + 8 ks .. + 7)
+//   qw:  f32 [r][rb][j / 4][64][4]: the head weight wv[rb][j] of each lane
+// The same launch clears the top-k histogram and candidate counts.
+template <int KK, int QK, int NQ>
+__global__ __launch_bounds__(256) void score_prep_kernel(ScoreParams p, uint32_t* cand_cnt) {
+  constexpr bool F16OP = (KK == KK_F16 || KK == KK_FP8);
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const int64_t n_clear = rows * HIST_BINS;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n_clear;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    p.hist[i] = 0;
+    if (i < rows) cand_cnt[i] = 0;
+  }
+  if (p.qop == nullptr) return;
+  const int lane = threadIdx.x & 63;
+  const int RB = p.H <= 32 ? 1 : 2;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wave >= rows * RB * 32) return;
+  const int64_t row = wave / (RB * 32);
+  const int h = static_cast<int>(wave - row * (RB * 32));
+  const int rb = h >> 5, hh = h & 31;
+  float x0 = 0.f, x1 = 0.f, wh = 0.f;
+  uint32_t raw = 0;
+  if (h < p.H) {
+    raw = reinterpret_cast<const uint32_t*>(p.q)[(row * p.H + h) * 64 + lane];
+    const uint16_t lo16 = raw & 0xffffu, hi16 = raw >> 16;
+    x0 = QK == 0 ? bf16_to_f32(lo16) : f16_to_f32(lo16);
+    x1 = QK == 0 ? bf16_to_f32(hi16) : f16_to_f32(hi16);
+    wh = p.w[row * p.H + h];
+  }
+  if (p.hadamard) {
+    {
+      const float u = x0, v = x1;
+      x0 = u + v;
+      x1 = u - v;
+    }
+#pragma unroll
+    for (int b = 1; b <= 32; b <<= 1) {   // the lower index keeps u + v, the upper u - v
+      const float o0 = __shfl_xor(x0, b, 64), o1 = __shfl_xor(x1, b, 64);
+      const bool up = (lane & b) != 0;
+      x0 = up ? o0 - x0 : x0 + o0;
+      x1 = up ? o1 - x1 : x1 + o1;
+      if (b == 32) {
+        x0 *= 0.088388347648318440550f;   // 1/sqrt(128)
+        x1 *= 0.088388347648318440550f;
+      }
+    }
+  }
+  uint32_t word[NQ];
+  float factor = 1.f;
+  if constexpr (F16OP) {
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    int e = 0;
+    if (amax > 0.f) {
+      int E;
+      frexpf(amax, &E);
+      e = 14 - E;   // amax * 2^e < 2^14: inside the f16 range with headroom
+    }
+    factor = ldexpf(1.f, -e);
+    word[0] = pack_f16x2(ldexpf(x0, e), ldexpf(x1, e));
+  } else if constexpr (QK == 0 && NQ == 1) {
+    word[0] = raw;   // bf16 q, used as it is
+  } else {
+    const float ah = bf16_to_f32(f32_to_bf16(x0)), bh = bf16_to_f32(f32_to_bf16(x1));
+    word[0] = pack_bf16x2(ah, bh);
+    word[NQ - 1] = pack_bf16x2(x0 - ah, x1 - bh);
+  }
+  if constexpr (KK == KK_FP8) factor *= 256.f;   // undo the 2^-8 of the fp8 -> f16 map
+  const float fw = wh * factor;
+  const int h2 = lane >> 5, ks = (lane & 31) >> 2, j = lane & 3;
+  uint32_t* qo = const_cast<uint32_t*>(p.qop) + row * (RB * 8 * NQ * 64 * 4);
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) qo[(((rb * 8 + ks) * NQ + nq) * 64 + hh + 32 * h2) * 4 + j] = word[nq];
+  if (lane < 32) {
+    float* qw = const_cast<float*>(p.qw) + row * (RB * 4 * 64 * 4);
+    const int hw2 = (hh >> 2) & 1;
+    qw[((rb * 4 + (hh >> 3)) * 64 + lane + 32 * hw2) * 4 + (hh & 3)] = fw;
+  }
+}
+
 // Decode variant (rows with the fused top-k histogram, 1- or 2-byte keys):
 // one wave per (query row, chunk of 32-key tiles), four chunks of one row per
 // workgroup, one wave per SIMD.  Each wave streams its own key tiles with
@@ -566,9 +657,33 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
     }
     if constexpr (KK == KK_FP8) tt.sc = sbase[ut + n < p.n_units ? ut + n : p.n_units - 1];
   };
-  // The first NR tiles of the chunk are requested before anything else (the
-  // visible length is not known yet: tiles past it are loaded, never used),
-  // so that the keys stream while q is loaded and converted.
+  // The prepared query operands and head weights are loaded first, then the
+  // first NR tiles of the chunk (the visible length is not known yet: tiles
+  // past it are loaded, never used).  Loads complete in issue order, so the
+  // products wait for the query alone while the keys stream.
+  u32x4_t qa[RB][8][NQ];
+  float wv[RB][16];
+  {
+    const u32x4_t* qo = reinterpret_cast<const u32x4_t*>(p.qop) + row * (RB * 8 * NQ * 64) + lane;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) qa[rb][ks][nq] = qo[((rb * 8 + ks) * NQ + nq) * 64];
+    const u32x4_t* wo = reinterpret_cast<const u32x4_t*>(p.qw) + row * (RB * 4 * 64) + lane;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const u32x4_t t = wo[(rb * 4 + jq) * 64];
+        wv[rb][4 * jq] = __uint_as_float(t.x);
+        wv[rb][4 * jq + 1] = __uint_as_float(t.y);
+        wv[rb][4 * jq + 2] = __uint_as_float(t.z);
+        wv[rb][4 * jq + 3] = __uint_as_float(t.w);
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   constexpr int NR = stream_occupancy<KK>() == 2 ? 2 : 4;
   StreamTile<KK> rr[NR];
   const int n_pre = active && chunk < tiles_row ? (tiles_row - chunk + p.n_chunks - 1) / p.n_chunks : 0;
@@ -579,9 +694,6 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
 
   const int32_t qpos = p.q_pos[row];
   const int64_t kl = p.kv_len ? p.kv_len[s] : p.n_units * p.c;
-  u32x4_t qa[RB][8][NQ];
-  float wv[RB][16];
-  query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
   for (int b = threadIdx.x; b < HIST_BINS; b += 256) s_hist[b] = 0;
 
   const int64_t n_vis = visible_tokens(qpos, kl, p.n_units * p.c) / p.c;
@@ -768,9 +880,62 @@ static bool scores_use_tiled(const ScoreParams& p) {
 }
 
 // the decode stream kernel covers 1- and 2-byte keys on rows with the histogram
+bool scores_use_prep(int q_dtype, int k_dtype, int H, int D, int64_t n_units) {
+  return scores_use_mfma(q_dtype, k_dtype, H, D) &&
+         (k_dtype == DSA_BF16 || k_dtype == DSA_F16 || k_dtype == DSA_FP8_E4M3) &&
+         n_units < (int64_t(1) << 24);   // 32-bit row offsets
+}
 static bool scores_use_stream(const ScoreParams& p) {
-  return (p.k_dtype == DSA_BF16 || p.k_dtype == DSA_F16 || p.k_dtype == DSA_FP8_E4M3) && p.hist != nullptr &&
-         p.chunk_major && p.chunk_tiles <= 32 && p.n_units < (int64_t(1) << 24);   // 32-bit row offsets
+  return p.hist != nullptr && p.qop != nullptr && p.chunk_major && p.chunk_tiles <= 32 &&
+         scores_use_prep(p.q_dtype, p.k_dtype, p.H, p.D, p.n_units);
+}
+
+// operand blocks of the stream kernel: RB head blocks, NQ operands per step
+static int prep_rb(int H) { return H <= 32 ? 1 : 2; }
+static int prep_nq(int q_dtype, int k_dtype, int hadamard) {
+  const bool f16op = k_dtype == DSA_F16 || k_dtype == DSA_FP8_E4M3;
+  return !f16op && (q_dtype != DSA_BF16 || hadamard) ? 2 : 1;
+}
+
+size_t score_prep_bytes(int64_t rows, int q_dtype, int k_dtype, int H, int hadamard) {
+  const size_t per_row = static_cast<size_t>(prep_rb(H)) * (8 * prep_nq(q_dtype, k_dtype, hadamard) + 4) * 64 * 16;
+  return (static_cast<size_t>(rows) * per_row + 255) / 256 * 256;
+}
+
+void score_prep_bind(ScoreParams& p, void* ws) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  const size_t ops = static_cast<size_t>(rows) * prep_rb(p.H) * 8 * prep_nq(p.q_dtype, p.k_dtype, p.hadamard) * 64 * 16;
+  p.qop = static_cast<const uint32_t*>(ws);
+  p.qw = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ops);
+}
+
+template <int KK>
+static hipError_t launch_prep_k(const ScoreParams& p, uint32_t* cand_cnt, dim3 grid, hipStream_t st) {
+  const bool nq2 = prep_nq(p.q_dtype, p.k_dtype, p.hadamard) == 2;
+  if (p.q_dtype == DSA_BF16) {
+    if (nq2) hipLaunchKernelGGL((score_prep_kernel<KK, 0, 2>), grid, dim3(256), 0, st, p, cand_cnt);
+    else hipLaunchKernelGGL((score_prep_kernel<KK, 0, 1>), grid, dim3(256), 0, st, p, cand_cnt);
+  } else {
+    if (nq2) hipLaunchKernelGGL((score_prep_kernel<KK, 1, 2>), grid, dim3(256), 0, st, p, cand_cnt);
+    else hipLaunchKernelGGL((score_prep_kernel<KK, 1, 1>), grid, dim3(256), 0, st, p, cand_cnt);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_prep(const ScoreParams& p, uint32_t* cand_cnt, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
+  int64_t blocks = (rows * HIST_BINS + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (p.qop != nullptr) {
+    const int64_t head_blocks = rows * prep_rb(p.H) * 32 / 4;
+    if (blocks < head_blocks) blocks = head_blocks;
+  }
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (p.k_dtype) {
+    case DSA_F16: return launch_prep_k<KK_F16>(p, cand_cnt, grid, st);
+    case DSA_FP8_E4M3: return launch_prep_k<KK_FP8>(p, cand_cnt, grid, st);
+    default: return launch_prep_k<KK_BF16>(p, cand_cnt, grid, st);
+  }
 }
 
 template <int KK, int QK, int NQ>
