@@ -1674,8 +1674,11 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
 constexpr size_t F32_LDS = 64 * 4 * 2 + 64 + MAX_BLOCKS * 4;
 
 // One wave per (query row, head, chunk).  64 tokens at a time: lane t scores
-// token t of the batch, the batch softmax updates the running state, then lane
-// t accumulates output dims t, t + 64, ...
+// token t of the batch (16-byte key loads when VEC: Dk and the strides are
+// multiples of 4), the batch softmax updates the running state, then lane t
+// accumulates output dims t, t + 64, ..., with the value loads of 8 tokens
+// issued before their products (which still add in token order).
+template <bool VEC>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t s_raw[];
   float* s_p = reinterpret_cast<float*>(s_raw);
@@ -1726,7 +1729,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     if (tok >= 0) {
       const float* kr = K + tok * p.k_tok;
       float d = 0.f;
-      for (int i = 0; i < p.Dk; ++i) d = fmaf(Q[i], kr[i], d);
+      if constexpr (VEC) {
+        for (int i = 0; i < p.Dk; i += 4) {
+          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(kr + i);
+          d = fmaf(Q[i], k4[0], d);
+          d = fmaf(Q[i + 1], k4[1], d);
+          d = fmaf(Q[i + 2], k4[2], d);
+          d = fmaf(Q[i + 3], k4[3], d);
+        }
+      } else {
+        for (int i = 0; i < p.Dk; ++i) d = fmaf(Q[i], kr[i], d);
+      }
       lg = d;
     }
     float tmax = lg;
@@ -1750,14 +1763,25 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     s_p[lane] = pr;
     s_t[lane] = static_cast<int32_t>(tok);
     __syncthreads();
-    for (int u = 0; u < 64; ++u) {
-      const int64_t tk = s_t[u];
-      if (tk < 0) continue;
-      const float* vr = V + tk * p.v_tok;
-      const float pu = s_p[u];
+    for (int u0 = 0; u0 < 64; u0 += 8) {
+      float vv[8][4], pu[8];
+      bool ok[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i < p.Dv) acc[i] = fmaf(pu, vr[lane + 64 * i], acc[i]);
+      for (int j = 0; j < 8; ++j) {
+        const int64_t tk = s_t[u0 + j];
+        ok[j] = tk >= 0;
+        pu[j] = s_p[u0 + j];
+        const float* vr = V + (ok[j] ? tk : 0) * p.v_tok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[j][i] = lane + 64 * i < p.Dv ? vr[lane + 64 * i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (!ok[j]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (lane + 64 * i < p.Dv) acc[i] = fmaf(pu[j], vv[j][i], acc[i]);
+      }
     }
     __syncthreads();
   }
@@ -1921,8 +1945,15 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
     hipLaunchKernelGGL(attn_gqa_kernel, dim3(static_cast<unsigned>(gqa_grid(p))), dim3(64), gqa_lds_bytes(p), st,
                        p);
   } else {
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(static_cast<unsigned>(rows * p.Hq * p.n_split)), dim3(64),
-                       F32_LDS, st, p);
+    // 16-byte key loads when every key row starts 16-byte aligned
+    const bool vec = p.Dk % 4 == 0 && p.k_tok % 4 == 0 && p.k_seq % 4 == 0 && p.k_head % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.k) & 15) == 0;
+    if (vec)
+      hipLaunchKernelGGL(attn_f32_kernel<true>, dim3(static_cast<unsigned>(rows * p.Hq * p.n_split)), dim3(64),
+                         F32_LDS, st, p);
+    else
+      hipLaunchKernelGGL(attn_f32_kernel<false>, dim3(static_cast<unsigned>(rows * p.Hq * p.n_split)), dim3(64),
+                         F32_LDS, st, p);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (before_combine && (e = hipEventRecord(before_combine, st)) != hipSuccess) return e;

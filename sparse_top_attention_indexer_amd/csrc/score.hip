@@ -815,9 +815,42 @@ __global__ __launch_bounds__(256, stream_occupancy<KK>()) void score_stream_kern
 }
 
 // Generic path: any element types, H <= 128, D <= 256.  One thread per
-// (row, unit); the row's (rotated) query and weights sit in LDS.
+// (row, unit); the row's (rotated) query and weights sit in LDS.  The key is
+// read once per group of 8 heads, in runs of 8 elements (16-byte loads when
+// D is a multiple of 8), and each run goes into every head of the group
+// before the next is read; each head's dot product still adds its terms in
+// dim order.
+template <int KD>
+__device__ __forceinline__ float key_elem(const void* k, int64_t i) {
+  return load_elem(k, i, KD);
+}
+template <int KD, bool VEC>
+__device__ __forceinline__ void key_run8(const void* k, int64_t i, float (&x)[8]) {
+  if constexpr (VEC && KD == DSA_F32) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(k) + i);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(k) + i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  } else if constexpr (VEC && (KD == DSA_BF16 || KD == DSA_F16)) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(k) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t lo = v[j] & 0xffffu, hi = v[j] >> 16;
+      x[2 * j] = KD == DSA_BF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
+      x[2 * j + 1] = KD == DSA_BF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = key_elem<KD>(k, i + j);
+  }
+}
+
+template <int KD, bool VEC>
 __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
-  extern __shared__ float s_q[];   // [H * D] then w[H]
+  extern __shared__ __align__(16) float s_q[];   // [H * D] then w[H]
   const int64_t n_ub = (p.n_units + 255) / 256;
   const int64_t row = blockIdx.x / n_ub;
   const int64_t ublk = blockIdx.x % n_ub;
@@ -848,13 +881,34 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
   float val = NEG_INF;
   if (u < n_vis) {
     const int64_t kb = (static_cast<int64_t>(s) * p.n_units + u) * D;
+    const int D8 = D & ~7;
     float tot = 0.f;
-    for (int h = 0; h < H; ++h) {
-      float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot = fmaf(s_q[h * D + d], load_elem(p.k, kb + d, p.k_dtype), dot);
-      tot = fmaf(s_w[h], fmaxf(dot, 0.f), tot);
+    for (int h0 = 0; h0 < H; h0 += 8) {
+      const int hn = H - h0 < 8 ? H - h0 : 8;   // heads of this group
+      float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int d0 = 0; d0 < D8; d0 += 8) {
+        float x[8];
+        key_run8<KD, VEC>(p.k, kb + d0, x);
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+          if (hh < hn) {
+            const float* qh = s_q + (h0 + hh) * D + d0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dot[hh] = fmaf(qh[j], x[j], dot[hh]);
+          }
+        }
+      }
+      for (int d = D8; d < D; ++d) {
+        const float xk = key_elem<KD>(p.k, kb + d);
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh)
+          if (hh < hn) dot[hh] = fmaf(s_q[(h0 + hh) * D + d], xk, dot[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh)
+        if (hh < hn) tot = fmaf(s_w[h0 + hh], fmaxf(dot[hh], 0.f), tot);
     }
-    if (p.k_dtype == DSA_FP8_E4M3) tot *= p.k_scale[static_cast<int64_t>(s) * p.n_units + u];
+    if (KD == DSA_FP8_E4M3) tot *= p.k_scale[static_cast<int64_t>(s) * p.n_units + u];
     val = tot;
   }
   p.scores[row * p.n_units + u] = val;
@@ -998,7 +1052,24 @@ hipError_t launch_scores(ScoreParams p, hipStream_t st) {
   if (!scores_use_mfma(p.q_dtype, p.k_dtype, p.H, p.D)) {
     const size_t lds = (static_cast<size_t>(p.H) * p.D + p.H) * sizeof(float);
     dim3 grid(static_cast<unsigned>(((p.n_units + 255) / 256) * rows));
-    hipLaunchKernelGGL(score_valu_kernel, grid, dim3(256), lds, st, p);
+    // 16-byte runs when every key row starts 16-byte aligned
+    const size_t esz = p.k_dtype == DSA_F32 ? 4 : (p.k_dtype == DSA_FP8_E4M3 ? 1 : 2);
+    const bool vec = p.D % 8 == 0 && (reinterpret_cast<uintptr_t>(p.k) & 15) == 0 && (p.D * esz) % 16 == 0;
+    switch (p.k_dtype) {
+      case DSA_F32:
+        if (vec) hipLaunchKernelGGL((score_valu_kernel<DSA_F32, true>), grid, dim3(256), lds, st, p);
+        else hipLaunchKernelGGL((score_valu_kernel<DSA_F32, false>), grid, dim3(256), lds, st, p);
+        break;
+      case DSA_BF16:
+        if (vec) hipLaunchKernelGGL((score_valu_kernel<DSA_BF16, true>), grid, dim3(256), lds, st, p);
+        else hipLaunchKernelGGL((score_valu_kernel<DSA_BF16, false>), grid, dim3(256), lds, st, p);
+        break;
+      case DSA_F16:
+        if (vec) hipLaunchKernelGGL((score_valu_kernel<DSA_F16, true>), grid, dim3(256), lds, st, p);
+        else hipLaunchKernelGGL((score_valu_kernel<DSA_F16, false>), grid, dim3(256), lds, st, p);
+        break;
+      default: hipLaunchKernelGGL((score_valu_kernel<DSA_FP8_E4M3, false>), grid, dim3(256), lds, st, p);
+    }
     return hipGetLastError();
   }
   const int64_t n_tiles = (p.n_units + 31) / 32;
