@@ -1676,10 +1676,11 @@ constexpr size_t F32_LDS = 64 * 4 * 2 + 64 + MAX_BLOCKS * 4;
 // One wave per (query row, head, chunk).  64 tokens at a time: lane t scores
 // token t of the batch (16-byte key loads when VEC: Dk and the strides are
 // multiples of 4), the batch softmax updates the running state, then lane t
-// accumulates output dims t, t + 64, ..., with the value loads of 8 tokens
+// accumulates output dims t, t + 64, ..., with the value loads of 32 tokens
 // issued before their products (which still add in token order).
 template <bool VEC>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
+  constexpr int VB = 32;   // tokens whose value loads are in flight together
   extern __shared__ __align__(16) uint8_t s_raw[];
   float* s_p = reinterpret_cast<float*>(s_raw);
   int32_t* s_t = reinterpret_cast<int32_t*>(s_p + 64);
@@ -1763,11 +1764,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     s_p[lane] = pr;
     s_t[lane] = static_cast<int32_t>(tok);
     __syncthreads();
-    for (int u0 = 0; u0 < 64; u0 += 8) {
-      float vv[8][4], pu[8];
-      bool ok[8];
+    for (int u0 = 0; u0 < 64; u0 += VB) {
+      float vv[VB][4], pu[VB];
+      bool ok[VB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < VB; ++j) {
         const int64_t tk = s_t[u0 + j];
         ok[j] = tk >= 0;
         pu[j] = s_p[u0 + j];
@@ -1776,7 +1777,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
         for (int i = 0; i < 4; ++i) vv[j][i] = lane + 64 * i < p.Dv ? vr[lane + 64 * i] : 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < VB; ++j) {
         if (!ok[j]) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
