@@ -629,6 +629,42 @@ def test_forward_decode_stream_matches_oracle(case):
     _end_to_end(wl, x, dev(x), [(s, 0) for s in range(wl.S)])
 
 
+PREP_CASES = {
+    # every operand form of the decode stream kernel's prepared queries:
+    # bf16 q used as it is, bf16 q rotated and split into two bf16 operands,
+    # f16 q prescaled for f16 keys, rotated bf16 / f16 q prescaled for fp8
+    # keys, one and two blocks of 32 heads (24 heads: the second half padded)
+    "bf16_q_bf16_keys": dict(k_dtype=torch.bfloat16, hadamard_q=False),
+    "bf16_q_bf16_keys_rotated_split": dict(k_dtype=torch.bfloat16, hadamard_q=True),
+    "bf16_q_f16_keys": dict(k_dtype=torch.float16, hadamard_q=False),
+    "bf16_q_fp8_keys_rotated": dict(k_dtype=torch.float8_e4m3fn, hadamard_q=True),
+    "f16_q_fp8_keys_rotated_24_heads": dict(k_dtype=torch.float8_e4m3fn, hadamard_q=True, q_dtype=torch.float16, H=24),
+    "f16_q_bf16_keys_48_heads": dict(k_dtype=torch.bfloat16, hadamard_q=False, q_dtype=torch.float16, H=48),
+}
+
+
+@pytest.mark.parametrize("case", list(PREP_CASES))
+def test_decode_stream_scores_bitwise_standalone(case):
+    """Decode rows score through score_prep_kernel's operands and the stream
+    kernel; the standalone call converts the same query in every wave of the
+    generic MFMA kernel, with the same products in the same order.  The two
+    score rows must agree bit for bit (the prep kernel's conversion is
+    query_operands' arithmetic, reordered only across lanes)."""
+    wl = replace(inputs.mini(3), name="prep_" + case, S=3, n_kv=9001, q_pos0=9000, seed=97, **PREP_CASES[case])
+    x = inputs.generate(wl)
+    d = dev(x)
+    _, _, scores = dsa.forward(d["Q"], d["K"], d["V"], d["q_idx"], d["k_idx"], d["w"], wl.top_k, wl.c, d["q_pos"],
+                               k_scale=d["k_scale"], n_sink=wl.n_sink, scale=wl.scale, hadamard_q=wl.hadamard_q,
+                               kv_len=d["kv_len"], return_idx=True, return_scores=True)
+    alone = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], d["q_pos"], k_scale=d["k_scale"], kv_len=d["kv_len"],
+                             hadamard_q=wl.hadamard_q)
+    torch.cuda.synchronize()
+    n_vis = int(x["kv_len"].min())
+    a = scores[..., :n_vis].contiguous().view(torch.int32)
+    b = alone[..., :n_vis].contiguous().view(torch.int32)
+    assert torch.equal(a, b), f"{case}: {int((a != b).sum())} scores differ"
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_forward_matches_oracle_full_size_sampled(n):
     """The full-size workloads, in the launch configuration the benchmark times,
