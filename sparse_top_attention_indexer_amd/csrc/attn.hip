@@ -171,6 +171,17 @@ __device__ __forceinline__ float quad_max(float x) {
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// IEEE maximum (NaN-propagating): no operand canonicalisation, and three
+// operands in one instruction on gfx950
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float quad_vmax(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float quad_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -1481,15 +1492,22 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
   const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
   const float c2 = p.scale_log2;
   const uint32_t vr_m = (lane >> 2) & 3, vr_r = lane & 3, vr_R = 4 * q + vr_m;
+  // V^T fragment db of lane (vr_R, vr_r): row vr_R, slot 2 (db ^ (vr_R & 7)) +
+  // vr_r / 2; the xor with 32 db only touches bits 5..7 of this offset (the
+  // buffer bases are multiples of 8 KB)
+  const uint32_t v_lane = vr_R * 256u + 32u * (vr_R & 7u) + 8u * vr_r;
+  // K fragment (mb, ks) of lane (col, q): row 16 mb + col, slot (4 ks + q) ^ col;
+  // (4 ks + q) ^ col = 4 ks ^ (q ^ col), so the offset is k_lane ^ 64 ks + 4096 mb
+  const uint32_t k_lane = static_cast<uint32_t>(col) * 256u + 16u * static_cast<uint32_t>(q ^ col);
 
   // O^T += V^T . P^T for the column groups in `cgs` (a pack of 0 / 1 flags)
   // with weights pw, straight-line: V^T fragments read two ahead, once per
   // tile for every group (attn_gqa_kernel's addressing)
   auto pv = [&](auto cgs, int bf, const u32x4_t (&pw)[GT_CG]) __attribute__((always_inline)) {
     constexpr int W0 = decltype(cgs)::value & 1, W1 = decltype(cgs)::value >> 1;
-    const uint8_t* vt_ = s_kv + bf * GT_BUF + GT_KV;
+    const uint32_t vt_off = static_cast<uint32_t>(bf * GT_BUF + GT_KV) + v_lane;
     auto vfrag = [&](int db) __attribute__((always_inline)) -> u32x4_t {
-      const uint8_t* a2 = vt_ + vr_R * 256 + 32 * (db ^ (vr_R & 7)) + 8 * vr_r;
+      const uint8_t* a2 = s_kv + (vt_off ^ (32u * db));
       const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a2);
       const v4i16_t vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a2 + 16 * 256));
       const u32x2_t u2 = __builtin_bit_cast(u32x2_t, va), w2 = __builtin_bit_cast(u32x2_t, vc);
@@ -1537,14 +1555,13 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
     for (int cg = 0; cg < GT_CG; ++cg) any = any || act[cg];
     if (!any) return;
     __builtin_amdgcn_s_setprio(2);   // the score chain and softmax first; other waves' products fill the gaps
-    const uint8_t* kt_ = s_kv + bf * GT_BUF;
-    // K fragment (mb, ks): tile row 16 mb + col, chunk 4 ks + q
+    const uint32_t kt_off = static_cast<uint32_t>(bf * GT_BUF) + k_lane;
     u32x4_t kf[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kf[mb][ks] = *reinterpret_cast<const u32x4_t*>(kt_ + (16 * mb + col) * 256 + 16 * ((4 * ks + q) ^ col));
+        kf[mb][ks] = *reinterpret_cast<const u32x4_t*>(s_kv + (kt_off ^ (64u * ks)) + 4096 * mb);
     u32x4_t ph[GT_CG], pl[GT_CG];
     bool lo[GT_CG];
 #pragma unroll
@@ -1570,9 +1587,8 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
           if (16 + j >= lim) s1[j] = NEG_INF;
         }
       }
-      float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-      tmax = quad_max(tmax);
+      float tmax = vmax3(vmax3(s0[0], s0[1], s0[2]), vmax3(s0[3], s1[0], s1[1]), vmax3(s1[2], s1[3], NEG_INF));
+      tmax = quad_vmax(tmax);
       tmax = mult[cg] != 0u ? tmax : NEG_INF;
       const bool first = m_run[cg] == NEG_INF;
       const bool grow = !first && (tmax - m_run[cg]) * c2 > 8.f;
@@ -1627,6 +1643,12 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
   // pair u - 2) also ends every wave's reads of those buffers.  Tile and
   // block ids are wave-uniform (scalar registers).
   const int tpb = blk ? p.c / TILE : 1;   // tiles per block
+  // kt / tpb for kt < 2^16 as the high word of kt * (floor(2^32 / tpb) + 1):
+  // the product overshoots kt / tpb by less than 2^-16 < 1 / tpb
+  const uint32_t tpb_m = tpb > 1 ? 0xffffffffu / static_cast<uint32_t>(tpb) + 1u : 0u;
+  auto block_of = [&](int kt) __attribute__((always_inline)) -> int {
+    return tpb > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(kt), tpb_m)) : kt;
+  };
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
     return kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s_tiles[u])));
   };
@@ -1638,10 +1660,10 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
     if (u + 2 < n_need) load_tile(tile_at(u + 2), (u + 2) % GT_NBUF);
     if (u + 3 < n_need) load_tile(tile_at(u + 3), (u + 3) % GT_NBUF);
     const int ka = tile_at(u);
-    compute(u % GT_NBUF, ka, ka / tpb);
+    compute(u % GT_NBUF, ka, block_of(ka));
     if (u + 1 < n_need) {
       const int kb_ = tile_at(u + 1);
-      compute((u + 1) % GT_NBUF, kb_, kb_ / tpb);
+      compute((u + 1) % GT_NBUF, kb_, block_of(kb_));
     }
   }
 
