@@ -1262,16 +1262,15 @@ __global__ __launch_bounds__(64, 2) void attn_gqa_kernel(AttnParams p) {
 // workgroup takes 128 / G consecutive queries of one sequence (G = heads per
 // group, a divisor of 16).
 constexpr int GT_WAVES = 8;
-constexpr int GT_CG = 1;                     // 16-column groups per wave
 constexpr int GT_NL = 8 / GT_WAVES;          // 1 KB K (and V) loads per wave and tile
 constexpr int GT_KV = TILE * GQA_D * 2;      // K (or V) rows of one tile of one group (8 KB)
 constexpr int GT_BUF = 2 * GT_KV;            // one tile: K rows, then V rows
 constexpr int GT_NBUF = 4;                   // a pair computed, a pair being loaded
-constexpr int GT_QMAX = GT_WAVES * GT_CG * 16;   // queries of a workgroup (G = 1)
+constexpr int GT_QMAX = GT_WAVES * 16;   // queries of a workgroup (G = 1)
 constexpr int GT_MAX_TILES = 2048;           // key tiles of one split
 constexpr int GT_MAX_CNT = 16384;            // (query, block) multiplicities in LDS (u16)
 
-static int gt_queries(const AttnParams& p) { return GT_WAVES * GT_CG * 16 / (p.Hq / p.Hkv); }
+static int gt_queries(const AttnParams& p) { return GT_WAVES * 16 / (p.Hq / p.Hkv); }
 static int64_t gt_blocks(const AttnParams& p) { return p.idx ? p.n_kv / p.c : 0; }
 
 // The query-tile kernel takes GQA calls in dense mode and in block mode with
@@ -1317,17 +1316,20 @@ static int64_t gt_grid(const AttnParams& p) {
 // gathered stream do; the summation runs in position order instead of list
 // order.  A tile lies in one block (32 | c), so its multiplicity per query
 // is one count, read from an LDS table built from the idx rows.
-//   scores  S^T (32 keys x 16 columns) = K_tile . Q^T, 16x16x32 MFMAs, K
-//           fragments read once per tile for both column groups
-//   softmax per column (attn_mla_kernel's lazy running max and bf16
-//           weights plus residual), masked entries -inf
-//   PV      O^T (128 dims x 16 columns) += V^T . P^T, V^T fragments through
-//           the transposing LDS read, once per tile for both groups
-// A column group whose queries all skip a tile skips its products.
+// Each wave holds 16 columns (query, head) and takes the tiles in pairs,
+// both tiles of a pair in one step:
+//   scores  S^T (32 keys x 16 columns) = K_tile . Q^T per tile, 16x16x32
+//           MFMAs, Q in registers
+//   softmax per column over the 64 keys of the pair (attn_mla_kernel's lazy
+//           running max and bf16 weights plus residual), masked entries -inf
+//   PV      O^T (128 dims x 16 columns) += V^T . P^T per tile, V^T fragments
+//           through the transposing LDS read
+// A wave whose columns all skip both tiles of a pair skips the step; a tile
+// of the step that every column skips gets zero weights.
 // K row t keeps 16-byte chunk c of its 256 bytes in slot c ^ (t & 15) and
 // V row t its 32-byte dim block b in slot b ^ (t & 7) (attn_gqa_kernel's V
 // layout): the fragment reads are free of bank conflicts.
-__global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnParams p) {
   constexpr int NT = 64 * GT_WAVES;
   extern __shared__ __align__(16) uint8_t s_raw[];
   uint8_t* s_kv = s_raw;                                                          // GT_NBUF tiles
@@ -1339,7 +1341,7 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = p.Hq / p.Hkv, QPC = 16 / G, QT = GT_WAVES * GT_CG * QPC;
+  const int G = p.Hq / p.Hkv, QPC = 16 / G, QT = GT_WAVES * QPC;
   const int64_t n_qt = (p.n_q + QT - 1) / QT;
   const int64_t b = blockIdx.x;
   int64_t unit;
@@ -1421,24 +1423,19 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
   __syncthreads();
   const int n_need = static_cast<int>(s_scr[8]);
 
-  // columns: group cg of wave wid holds queries (GT_CG wid + cg) QPC .. of the
-  // tile, G heads each; lane (col, q) holds column col
+  // columns: wave wid holds queries wid QPC .. wid QPC + QPC - 1 of the tile,
+  // G heads each; lane (col, q) holds column col
   const int col = lane & 15, q = lane >> 4;
-  u32x4_t qf[GT_CG][4];
-  int32_t c_qi[GT_CG], c_nv[GT_CG], c_tl[GT_CG];
-  bool c_ok[GT_CG];
   const int head = g * G + col % G;
-#pragma unroll
-  for (int cg = 0; cg < GT_CG; ++cg) {
-    const int qi = (wid * GT_CG + cg) * QPC + col / G;
-    c_qi[cg] = qi;
-    c_ok[cg] = qi < nqt;
-    c_nv[cg] = s_nv[qi];
-    c_tl[cg] = s_tl[qi];
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((row0 + (c_ok[cg] ? qi : 0)) * p.Hq + head) * GQA_D;
+  const int qi = wid * QPC + col / G;
+  const bool c_ok = qi < nqt;
+  const int32_t c_nv = s_nv[qi], c_tl = s_tl[qi];
+  u32x4_t qf[4];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((row0 + (c_ok ? qi : 0)) * p.Hq + head) * GQA_D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qf[cg][ks] = c_ok[cg] ? *reinterpret_cast<const u32x4_t*>(qr + 32 * ks + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+      qf[ks] = c_ok ? *reinterpret_cast<const u32x4_t*>(qr + 32 * ks + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
   // tile loads: wave w, load i copies tile rows 4 (2 w + i) .. + 3 (1 KB of
@@ -1477,18 +1474,14 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
     }
   };
 
-  // o[cg][db], db < 8: dims 16 db + 4 q + j of column col (O^T); o[cg][8]:
-  // the column's normaliser in every register, as the product of the
-  // weights with a block of ones, so that it sums exactly the bf16 weights
-  // the value products take
-  f32x4_t o[GT_CG][9];
+  // o[db], db < 8: dims 16 db + 4 q + j of column col (O^T); o[8]: the
+  // column's normaliser in every register, as the product of the weights
+  // with a block of ones, so that it sums exactly the bf16 weights the value
+  // products take
+  f32x4_t o[9];
 #pragma unroll
-  for (int cg = 0; cg < GT_CG; ++cg)
-#pragma unroll
-    for (int db = 0; db < 9; ++db) o[cg][db] = f32x4_t{};
-  float m_run[GT_CG];
-#pragma unroll
-  for (int cg = 0; cg < GT_CG; ++cg) m_run[cg] = NEG_INF;
+  for (int db = 0; db < 9; ++db) o[db] = f32x4_t{};
+  float m_run = NEG_INF;
   const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
   const float c2 = p.scale_log2;
   const uint32_t vr_m = (lane >> 2) & 3, vr_r = lane & 3, vr_R = 4 * q + vr_m;
@@ -1500,14 +1493,15 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
   // (4 ks + q) ^ col = 4 ks ^ (q ^ col), so the offset is k_lane ^ 64 ks + 4096 mb
   const uint32_t k_lane = static_cast<uint32_t>(col) * 256u + 16u * static_cast<uint32_t>(q ^ col);
 
-  // O^T += V^T . P^T for the column groups in `cgs` (a pack of 0 / 1 flags)
-  // with weights pw, straight-line: V^T fragments read two ahead, once per
-  // tile for every group (attn_gqa_kernel's addressing)
-  auto pv = [&](auto cgs, int bf, const u32x4_t (&pw)[GT_CG]) __attribute__((always_inline)) {
-    constexpr int W0 = decltype(cgs)::value & 1, W1 = decltype(cgs)::value >> 1;
-    const uint32_t vt_off = static_cast<uint32_t>(bf * GT_BUF + GT_KV) + v_lane;
-    auto vfrag = [&](int db) __attribute__((always_inline)) -> u32x4_t {
-      const uint8_t* a2 = s_kv + (vt_off ^ (32u * db));
+  // O^T += V^T . P^T over the N tiles in buffers bf[0..N-1], weights pw[i],
+  // straight-line: the normaliser first, then tile 0's 8 dim blocks, then
+  // tile 1's (so each accumulator's two products are 8 apart), V^T fragments
+  // read two ahead (attn_gqa_kernel's addressing)
+  auto pv = [&](auto n_t, const int (&bf)[2], const u32x4_t (&pw)[2]) __attribute__((always_inline)) {
+    constexpr int N = decltype(n_t)::value;
+    auto vfrag = [&](int e) __attribute__((always_inline)) -> u32x4_t {
+      const uint32_t vt_off = static_cast<uint32_t>(bf[e / 8] * GT_BUF + GT_KV) + v_lane;
+      const uint8_t* a2 = s_kv + (vt_off ^ (32u * (e % 8)));
       const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a2);
       const v4i16_t vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a2 + 16 * 256));
       const u32x2_t u2 = __builtin_bit_cast(u32x2_t, va), w2 = __builtin_bit_cast(u32x2_t, vc);
@@ -1516,132 +1510,128 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
     constexpr int VD = 2;
     u32x4_t vf[VD];
 #pragma unroll
-    for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
-    if constexpr (W0 != 0) o[0][8] = mfma16x16x32_bf16(ones, pw[0], o[0][8]);
-    if constexpr (W1 != 0 && GT_CG > 1) o[GT_CG - 1][8] = mfma16x16x32_bf16(ones, pw[GT_CG - 1], o[GT_CG - 1][8]);
+    for (int e = 0; e < VD; ++e) vf[e] = vfrag(e);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      if constexpr (W0 != 0) o[0][db] = mfma16x16x32_bf16(vf[db % VD], pw[0], o[0][db]);
-      if constexpr (W1 != 0 && GT_CG > 1) o[GT_CG - 1][db] = mfma16x16x32_bf16(vf[db % VD], pw[GT_CG - 1], o[GT_CG - 1][db]);
-      if (db + VD < 8) vf[db % VD] = vfrag(db + VD);
+    for (int i = 0; i < N; ++i) o[8] = mfma16x16x32_bf16(ones, pw[i], o[8]);
+#pragma unroll
+    for (int e = 0; e < 8 * N; ++e) {
+      o[e % 8] = mfma16x16x32_bf16(vf[e % VD], pw[e / 8], o[e % 8]);
+      if (e + VD < 8 * N) vf[e % VD] = vfrag(e + VD);
     }
   };
-  using both_t = std::integral_constant<int, 3>;
-  using first_t = std::integral_constant<int, 1>;
-  using second_t = std::integral_constant<int, 2>;
 
-  // the multiplicity table's row of each column's query
-  int32_t c_cb[GT_CG];
-#pragma unroll
-  for (int cg = 0; cg < GT_CG; ++cg) c_cb[cg] = c_qi[cg] * nb;
-  auto compute = [&](int bf, int kt, int bl) __attribute__((always_inline)) {
+  // the column's multiplicity for key tile kt of block bl: 0 when its query
+  // skips the tile
+  const int32_t c_cb = qi * nb;   // the query's row of the multiplicity table
+  auto tile_mult = [&](int kt, int bl) __attribute__((always_inline)) -> uint32_t {
     const int t0 = kt * TILE;
-    const int blc = bl < nb ? bl : nb - 1;   // a tile past the complete blocks is every query's tail
-    uint32_t mult[GT_CG];
-    bool act[GT_CG];
-#pragma unroll
-    for (int cg = 0; cg < GT_CG; ++cg) {
-      uint32_t cnt = 1u;
-      if (nb > 0) {
-        const uint32_t at = static_cast<uint32_t>(c_cb[cg] + blc);
-        cnt = (s_cnt[at >> 1] >> (16 * (at & 1))) & 0xffffu;
-      }
-      const bool vis = c_ok[cg] && t0 < c_nv[cg];
-      mult[cg] = vis ? (t0 >= c_tl[cg] ? 1u : cnt) : 0u;
-      act[cg] = __ballot(mult[cg] != 0u) != 0;
+    uint32_t cnt = 1u;
+    if (nb > 0) {
+      const int blc = bl < nb ? bl : nb - 1;   // a tile past the complete blocks is every query's tail
+      const uint32_t at = static_cast<uint32_t>(c_cb + blc);
+      cnt = (s_cnt[at >> 1] >> (16 * (at & 1))) & 0xffffu;
     }
-    bool any = false;
-#pragma unroll
-    for (int cg = 0; cg < GT_CG; ++cg) any = any || act[cg];
-    if (!any) return;
+    const bool vis = c_ok && t0 < c_nv;
+    return vis ? (t0 >= c_tl ? 1u : cnt) : 0u;
+  };
+
+  // One online-softmax step over N = 1 or 2 tiles (buffers bf, key tiles kt,
+  // multiplicities mult) that some column of the wave attends to: the scores
+  // of all N tiles, one running-max update and one residual decision, then
+  // the value products of the N tiles in position order.
+  auto step = [&](auto n_t, const int (&bf)[2], const int (&kt)[2], const uint32_t (&mult)[2])
+                  __attribute__((always_inline)) {
+    constexpr int N = decltype(n_t)::value;
     __builtin_amdgcn_s_setprio(2);   // the score chain and softmax first; other waves' products fill the gaps
-    const uint32_t kt_off = static_cast<uint32_t>(bf * GT_BUF) + k_lane;
-    u32x4_t kf[2][4];
+    // reg j of s[i][mb]: key 32 kt[i] + 16 mb + 4 q + j of column col
+    f32x4_t s[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < N; ++i) {
+      const uint32_t kt_off = static_cast<uint32_t>(bf[i] * GT_BUF) + k_lane;
+      s[i][0] = s[i][1] = f32x4_t{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kf[mb][ks] = *reinterpret_cast<const u32x4_t*>(s_kv + (kt_off ^ (64u * ks)) + 4096 * mb);
-    u32x4_t ph[GT_CG], pl[GT_CG];
-    bool lo[GT_CG];
 #pragma unroll
-    for (int cg = 0; cg < GT_CG; ++cg) {
-      lo[cg] = false;
-      ph[cg] = pl[cg] = u32x4_t{0u, 0u, 0u, 0u};
-      if (!act[cg]) continue;
-      f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+        for (int mb = 0; mb < 2; ++mb)
+          s[i][mb] = mfma16x16x32_bf16(*reinterpret_cast<const u32x4_t*>(s_kv + (kt_off ^ (64u * ks)) + 4096 * mb),
+                                       qf[ks], s[i][mb]);
+    }
+    // A column whose query skips a tile (mult 0) keeps that tile's scores out
+    // of the max and gets zero weights through an infinite offset; keys past a
+    // query's last visible token (only in a tile that crosses it) are -inf.
+    float tmax = NEG_INF;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s0 = mfma16x16x32_bf16(kf[0][ks], qf[cg][ks], s0);
-        s1 = mfma16x16x32_bf16(kf[1][ks], qf[cg][ks], s1);
-      }
-      // reg j of s_mb: key t0 + 16 mb + 4 q + j of column col.  A column whose
-      // query skips the tile (mult 0) keeps its scores out of the max and
-      // gets zero weights through an infinite offset; keys past a query's
-      // last visible token (only in a tile that crosses it) are -inf.
-      const int lim = c_nv[cg] - t0 - 4 * q;   // keys j < lim (+ 16 mb) are visible
-      if (__ballot(mult[cg] != 0u && t0 + TILE > c_nv[cg]) != 0) {
+    for (int i = 0; i < N; ++i) {
+      const int t0 = kt[i] * TILE;
+      if (__ballot(mult[i] != 0u && t0 + TILE > c_nv) != 0) {
+        const int lim = c_nv - t0 - 4 * q;   // keys j < lim (+ 16 mb) are visible
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (j >= lim) s0[j] = NEG_INF;
-          if (16 + j >= lim) s1[j] = NEG_INF;
+          if (j >= lim) s[i][0][j] = NEG_INF;
+          if (16 + j >= lim) s[i][1][j] = NEG_INF;
         }
       }
-      float tmax = vmax3(vmax3(s0[0], s0[1], s0[2]), vmax3(s0[3], s1[0], s1[1]), vmax3(s1[2], s1[3], NEG_INF));
-      tmax = quad_vmax(tmax);
-      tmax = mult[cg] != 0u ? tmax : NEG_INF;
-      const bool first = m_run[cg] == NEG_INF;
-      const bool grow = !first && (tmax - m_run[cg]) * c2 > 8.f;
-      const float a = __builtin_amdgcn_exp2f((m_run[cg] - tmax) * c2);
-      const float alpha = grow ? a : 1.f;
-      m_run[cg] = (first || grow) ? tmax : m_run[cg];
-      float mb_ = m_run[cg] == NEG_INF ? 0.f : m_run[cg] * c2;
-      // the multiplicity scales the weights: offset log2(mult), zero -> +inf
-      if (__ballot(mult[cg] > 1u) != 0) mb_ -= __builtin_amdgcn_logf(static_cast<float>(mult[cg] > 1u ? mult[cg] : 1u));
-      mb_ = mult[cg] != 0u ? mb_ : __builtin_inff();
+      const float t = vmax3(vmax3(s[i][0][0], s[i][0][1], s[i][0][2]), vmax3(s[i][0][3], s[i][1][0], s[i][1][1]),
+                            vmax3(s[i][1][2], s[i][1][3], NEG_INF));
+      tmax = mult[i] != 0u ? __builtin_elementwise_maximum(tmax, t) : tmax;
+    }
+    tmax = quad_vmax(tmax);
+    const bool first = m_run == NEG_INF;
+    const bool grow = !first && (tmax - m_run) * c2 > 8.f;
+    const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
+    const float alpha = grow ? a : 1.f;
+    m_run = (first || grow) ? tmax : m_run;
+    const float mc = m_run == NEG_INF ? 0.f : m_run * c2;
+    // the multiplicity scales the weights: offset log2(mult), zero -> +inf
+    float mo[2];
+    float mo_min = __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      mo[i] = mc;
+      if (__ballot(mult[i] > 1u) != 0) mo[i] -= __builtin_amdgcn_logf(static_cast<float>(mult[i] > 1u ? mult[i] : 1u));
+      mo[i] = mult[i] != 0u ? mo[i] : __builtin_inff();
+      mo_min = fminf(mo_min, mo[i]);
+    }
+    // the step adds at least its largest weight (at most this bound) to the
+    // rescaled normaliser
+    const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mo_min));
+    const bool lo = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[8][0] * alpha) != 0;
+    u32x4_t ph[2], pl[2];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
       float x[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -mb_));
-        x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -mb_));
+        x[j] = __builtin_amdgcn_exp2f(fmaf(s[i][0][j], c2, -mo[i]));
+        x[4 + j] = __builtin_amdgcn_exp2f(fmaf(s[i][1][j], c2, -mo[i]));
       }
-      uint32_t hv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-      ph[cg] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
-      // the tile adds at least its largest weight to the rescaled normaliser
-      const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb_));
-      lo[cg] = __ballot(xmax * (1.f - LO_SHARE) > LO_SHARE * o[cg][8][0] * alpha) != 0;
-      if (lo[cg]) {
+      ph[i] = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      if (lo) {
         uint32_t lv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          lv[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hv[i] << 16), x[2 * i + 1] - __uint_as_float(hv[i] & 0xffff0000u));
-        pl[cg] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t hv = ph[i][k];
+          lv[k] = pack_bf16x2(x[2 * k] - __uint_as_float(hv << 16), x[2 * k + 1] - __uint_as_float(hv & 0xffff0000u));
+        }
+        pl[i] = u32x4_t{lv[0], lv[1], lv[2], lv[3]};
       }
-      if (__ballot(alpha != 1.f) != 0) {
+    }
+    if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-        for (int db = 0; db < 9; ++db) o[cg][db] *= alpha;
-      }
+      for (int db = 0; db < 9; ++db) o[db] *= alpha;
     }
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (GT_CG == 2) {
-      if (act[0] && act[1]) pv(both_t{}, bf, ph);
-      else if (act[0]) pv(first_t{}, bf, ph);
-      else pv(second_t{}, bf, ph);
-      if (lo[0] && lo[1]) pv(both_t{}, bf, pl);
-      else if (lo[0]) pv(first_t{}, bf, pl);
-      else if (lo[1]) pv(second_t{}, bf, pl);
-    } else {
-      pv(first_t{}, bf, ph);
-      if (lo[0]) pv(first_t{}, bf, pl);
-    }
+    pv(n_t, bf, ph);
+    if (lo) pv(n_t, bf, pl);
   };
+  using two_t = std::integral_constant<int, 2>;
 
   // pipeline over pairs of tiles: the loads of pair u + 2, u + 3 run while
   // pair u, u + 1 is computed; the barrier before them (into the buffers of
   // pair u - 2) also ends every wave's reads of those buffers.  Tile and
-  // block ids are wave-uniform (scalar registers).
+  // block ids are wave-uniform (scalar registers).  A wave attending to both
+  // tiles of a pair takes them in one step (the two tiles of a block of 64
+  // share every query's multiplicity), else the one it attends to.
   const int tpb = blk ? p.c / TILE : 1;   // tiles per block
   // kt / tpb for kt < 2^16 as the high word of kt * (floor(2^32 / tpb) + 1):
   // the product overshoots kt / tpb by less than 2^-16 < 1 / tpb
@@ -1660,32 +1650,38 @@ __global__ __launch_bounds__(64 * GT_WAVES, 2) void attn_gqa_tile_kernel(AttnPar
     if (u + 2 < n_need) load_tile(tile_at(u + 2), (u + 2) % GT_NBUF);
     if (u + 3 < n_need) load_tile(tile_at(u + 3), (u + 3) % GT_NBUF);
     const int ka = tile_at(u);
-    compute(u % GT_NBUF, ka, block_of(ka));
+    const uint32_t ma = tile_mult(ka, block_of(ka));
+    const bool aa = __ballot(ma != 0u) != 0;
+    int kb_ = ka;
+    uint32_t mb_ = 0u;
+    bool ab = false;
     if (u + 1 < n_need) {
-      const int kb_ = tile_at(u + 1);
-      compute((u + 1) % GT_NBUF, kb_, block_of(kb_));
+      kb_ = tile_at(u + 1);
+      mb_ = tile_mult(kb_, block_of(kb_));
+      ab = __ballot(mb_ != 0u) != 0;
     }
+    // a pair without a second tile takes the first tile's buffer with
+    // multiplicity 0 for every column (finite scores, zero weights)
+    const int bfa = u % GT_NBUF, bfb = u + 1 < n_need ? (u + 1) % GT_NBUF : bfa;
+    if (aa || ab) step(two_t{}, {bfa, bfb}, {ka, kb_}, {ma, mb_});
   }
 
-  // output: accumulator (cg, db, j) holds dim 16 db + 4 q + j of column col
-#pragma unroll
-  for (int cg = 0; cg < GT_CG; ++cg) {
-    if (!c_ok[cg]) continue;
-    const int64_t row = row0 + c_qi[cg];
+  // output: accumulator (db, j) holds dim 16 db + 4 q + j of column col
+  if (c_ok) {
+    const int64_t row = row0 + qi;
     if (p.n_split == 1) {
-      const float inv = o[cg][8][0] > 0.f ? 1.f / o[cg][8][0] : 0.f;
+      const float inv = o[8][0] > 0.f ? 1.f / o[8][0] : 0.f;
       const int64_t ob = (row * p.Hq + head) * GQA_D + 4 * q;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        store4(p.out, p.o_dtype, ob + 16 * db, o[cg][db][0] * inv, o[cg][db][1] * inv, o[cg][db][2] * inv,
-               o[cg][db][3] * inv);
+        store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
     } else {
       float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(GQA_D);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[cg][db];
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
       if (q == 0) {
-        pp[GQA_D] = m_run[cg];
-        pp[GQA_D + 1] = o[cg][8][0];
+        pp[GQA_D] = m_run;
+        pp[GQA_D + 1] = o[8][0];
       }
     }
   }
