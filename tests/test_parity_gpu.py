@@ -746,3 +746,38 @@ def test_gqa_block_mode_list_order_repeats_and_dead_rows():
         assert np.all(got[1, 5] == 0.0)
     print(f"gqa block mode, shuffled and repeated lists: max |O - oracle| {worst:.2e}")
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("c", [32, 96, 128])
+def test_gqa_query_tiles_block_sizes(c):
+    # the query-tile GQA kernel at block sizes of 1, 3 and 4 key tiles: with
+    # blocks of one tile the two tiles of a step belong to different blocks
+    # (different multiplicities per query); with three the block of a tile
+    # comes from the multiply-high division.  37 rows (ragged query tiles),
+    # two sequences with different stored lengths, and lists with every row's
+    # blocks shuffled and one block listed twice.
+    wl = replace(inputs.mini(4), name="qsa_tiles_c", S=2, n_q=37, n_kv=3000, q_pos0=2963, c=c, top_k=10 * c)
+    x = inputs.generate(wl, seed=200 + c)
+    x["kv_len"] = torch.tensor([3000, 2700], dtype=torch.int32)
+    d = dev(x)
+    qp, kv = x["q_pos"].numpy(), x["kv_len"].numpy()
+    ref_idx, _ = _oracle_idx(x, wl)
+    rng = np.random.default_rng(c)
+    mixed = ref_idx.copy()
+    for s in range(wl.S):
+        for i in range(wl.n_q):
+            row = mixed[s, i]
+            live = row[row >= 0]
+            if live.size >= 2:
+                perm = rng.permutation(live)
+                perm[-1] = perm[0]
+                row[:] = -1
+                row[:live.size] = perm
+    worst = 0.0
+    for idx in (ref_idx, mixed):
+        got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"], torch.from_numpy(idx.astype(np.int32)).to(DEV),
+                              c=wl.c, kv_len=d["kv_len"], scale=wl.scale).cpu().double().numpy()
+        ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), idx, qp, kv, wl.c, wl.scale)
+        worst = max(worst, float(np.abs(got - ref).max()))
+    print(f"gqa query tiles, blocks of {c}: max |O - oracle| {worst:.2e}")
+    assert worst <= 2e-2
