@@ -1545,17 +1545,21 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
     __builtin_amdgcn_s_setprio(2);   // the score chain and softmax first; other waves' products fill the gaps
     // reg j of s[i][mb]: key 32 kt[i] + 16 mb + 4 q + j of column col
     f32x4_t s[2][2];
+    uint32_t kt_off[2];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint32_t kt_off = static_cast<uint32_t>(bf[i] * GT_BUF) + k_lane;
+      kt_off[i] = static_cast<uint32_t>(bf[i] * GT_BUF) + k_lane;
       s[i][0] = s[i][1] = f32x4_t{};
+    }
+    // the N x 2 accumulation chains interleaved, step ks of every chain in turn
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          s[i][mb] = mfma16x16x32_bf16(*reinterpret_cast<const u32x4_t*>(s_kv + (kt_off ^ (64u * ks)) + 4096 * mb),
+          s[i][mb] = mfma16x16x32_bf16(*reinterpret_cast<const u32x4_t*>(s_kv + (kt_off[i] ^ (64u * ks)) + 4096 * mb),
                                        qf[ks], s[i][mb]);
-    }
     // A column whose query skips a tile (mult 0) keeps that tile's scores out
     // of the max and gets zero weights through an infinite offset; keys past a
     // query's last visible token (only in a tile that crosses it) are -inf.
