@@ -210,6 +210,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 // products.  Tiles are gathered with direct global -> LDS loads two
 // segments ahead (three tile buffers).  Token ids of the stream sit in an LDS
 // ring of 32 tiles, refilled 16 tiles ahead.
+template <bool HG64>
 __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams p) {
   constexpr int NW = MLA_WAVES;
   constexpr int GW = NW / 2;   // waves per group
@@ -227,8 +228,15 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   const int s = static_cast<int>(row / p.n_q);
   const int grp = wid / GW;
   const int col = lane & 15, q = lane >> 4;
-  const int head0 = blockIdx.y * (16 * NW) + wid * 16;
-  const bool wvalid = head0 < p.Hq;   // Hq is a multiple of 16
+  // Heads per workgroup: 128 (16 a wave), or 64 (HG64) when few rows would
+  // leave CUs idle.  Then waves 0, 1 (first group) and 6, 7 (second group)
+  // hold the heads, one per SIMD (waves w and w + 4 share one), and the
+  // other four only gather and synchronise.  A head's arithmetic does not
+  // depend on the workgroup that computes it.
+  const bool has_heads = !HG64 || wid < 2 || wid >= 6;
+  const int slot = HG64 ? (wid < 2 ? wid : wid - 4) : wid;
+  const int head0 = blockIdx.y * (HG64 ? 64 : 16 * NW) + slot * 16;
+  const bool wvalid = has_heads && head0 < p.Hq;   // Hq is a multiple of 16
   const int head = head0 + col;
 
   // In token mode the stream is the idx row itself (its length k_sel needs no
@@ -408,6 +416,15 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
       }
     }
   };
+  // a wave without heads (64-head workgroups): its share of the gather alone
+  auto gather_only = [&](auto plan, int32_t tl, int bg) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t lb = kb_lds + bg * KT_BYTES;
+    constexpr int NL = decltype(plan)::value == 1 ? N_MAIN + N_ROPE : N_MAIN;
+#pragma unroll
+    for (int c = 0; c < NL; ++c) gather_c(plan, c, tl, lb, ln);
+  };
   // softmax: s_mb reg j holds key 16 mb + 4 q + j of head col.  Produces the
   // P^T fragments (k slot j < 4: key 4 q + j; j >= 4: key 16 + 4 q + j - 4)
   // and returns the factor that rescales what was accumulated before.
@@ -584,35 +601,47 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
 
   // Segment sg: waves 0..3 compute the scores and softmax of tile sg / 2
   // (even sg) or its PV products (odd sg); waves 4..7 do the same one segment
-  // later.  Waves without
-  // heads (Hq < 128) run the same products on head 0's query, so that
-  // every wave takes the same straight-line path.
+  // later.  Waves without heads in a 128-head workgroup (Hq < 128) run the
+  // same products on head 0's query, so that every wave takes the same
+  // straight-line path; in a 64-head workgroup the four waves without heads
+  // run a loop of their own that issues their gather share and meets the
+  // same barriers.
   using plan_hi = std::integral_constant<int, 1>;   // the gather share of waves 4..7
   using plan_lo = std::integral_constant<int, 2>;   // the gather share of waves 0..3
   if (grp == 0) {
-    for (int u = 0; u < n_tiles; ++u) {
-      segment_io(2 * u);
-      f32x4_t s0, s1;
-      u32x4_t ph, pl;
-      bool need_lo;
-      float mb;
-      // tile u + 1 past tile 1 (the first two come whole from the prologue;
-      // at u = 0 this reloads rows of tile 1 with the same bytes, and past
-      // the stream it loads rows nothing reads)
-      __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
-      scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), (u + 1) % KT_NBUF);
-      rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
-      __builtin_amdgcn_s_setprio(0);
-      segment_end(2 * u);
-      segment_io(2 * u + 1);
-      softmax_b(s0, s1, mb, need_lo, ph, pl);
-      u32x4_t pw = ph;
+    if (!HG64 || has_heads) {
+      for (int u = 0; u < n_tiles; ++u) {
+        segment_io(2 * u);
+        f32x4_t s0, s1;
+        u32x4_t ph, pl;
+        bool need_lo;
+        float mb;
+        // tile u + 1 past tile 1 (the first two come whole from the prologue;
+        // at u = 0 this reloads rows of tile 1 with the same bytes, and past
+        // the stream it loads rows nothing reads)
+        __builtin_amdgcn_s_setprio(2);   // the score chain first; the other group's PV fills the gaps
+        scores(plan_lo{}, u % KT_NBUF, s0, s1, tokens_of(u + 1), (u + 1) % KT_NBUF);
+        rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
+        __builtin_amdgcn_s_setprio(0);
+        segment_end(2 * u);
+        segment_io(2 * u + 1);
+        softmax_b(s0, s1, mb, need_lo, ph, pl);
+        u32x4_t pw = ph;
 #pragma clang loop unroll(disable)
-      for (int ps = 0; ps < 1 + need_lo; ++ps) {
-        pv(u % KT_NBUF, pw);
-        pw = pl;
+        for (int ps = 0; ps < 1 + need_lo; ++ps) {
+          pv(u % KT_NBUF, pw);
+          pw = pl;
+        }
+        segment_end(2 * u + 1);
       }
-      segment_end(2 * u + 1);
+    } else {
+      for (int u = 0; u < n_tiles; ++u) {
+        segment_io(2 * u);
+        gather_only(plan_lo{}, tokens_of(u + 1), (u + 1) % KT_NBUF);
+        segment_end(2 * u);
+        segment_io(2 * u + 1);
+        segment_end(2 * u + 1);
+      }
     }
     // the last segment is the other group's last PV: this group's outputs
     // are final and are written meanwhile
@@ -622,30 +651,41 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
   } else {
     segment_io(0);
     segment_end(0);
-    for (int u = 0; u < n_tiles; ++u) {
-      // the gather of tile u + 2 also runs past the end: it then reloads rows
-      // (ring entries past the stream: token 0 or stale valid ids) into the
-      // buffer of tile u - 1, which nothing reads again
-      segment_io(2 * u + 1);
-      f32x4_t s0, s1;
-      u32x4_t ph, pl;
-      bool need_lo;
-      float mb;
-      __builtin_amdgcn_s_setprio(2);
-      scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, (u + 2) % KT_NBUF);
-      rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
-      __builtin_amdgcn_s_setprio(0);
-      segment_end(2 * u + 1);
-      segment_io(2 * u + 2);
-      g_tl = tokens_of(u + 3);   // for the next score segment
-      softmax_b(s0, s1, mb, need_lo, ph, pl);
-      u32x4_t pw = ph;
+    if (!HG64 || has_heads) {
+      for (int u = 0; u < n_tiles; ++u) {
+        // the gather of tile u + 2 also runs past the end: it then reloads rows
+        // (ring entries past the stream: token 0 or stale valid ids) into the
+        // buffer of tile u - 1, which nothing reads again
+        segment_io(2 * u + 1);
+        f32x4_t s0, s1;
+        u32x4_t ph, pl;
+        bool need_lo;
+        float mb;
+        __builtin_amdgcn_s_setprio(2);
+        scores(plan_hi{}, u % KT_NBUF, s0, s1, g_tl, (u + 2) % KT_NBUF);
+        rescale(softmax_a(s0, s1, live_of(u), mb, need_lo));
+        __builtin_amdgcn_s_setprio(0);
+        segment_end(2 * u + 1);
+        segment_io(2 * u + 2);
+        g_tl = tokens_of(u + 3);   // for the next score segment
+        softmax_b(s0, s1, mb, need_lo, ph, pl);
+        u32x4_t pw = ph;
 #pragma clang loop unroll(disable)
-      for (int ps = 0; ps < 1 + need_lo; ++ps) {
-        pv(u % KT_NBUF, pw);
-        pw = pl;
+        for (int ps = 0; ps < 1 + need_lo; ++ps) {
+          pv(u % KT_NBUF, pw);
+          pw = pl;
+        }
+        segment_end(2 * u + 2);
       }
-      segment_end(2 * u + 2);
+    } else {
+      for (int u = 0; u < n_tiles; ++u) {
+        segment_io(2 * u + 1);
+        gather_only(plan_hi{}, g_tl, (u + 2) % KT_NBUF);
+        segment_end(2 * u + 1);
+        segment_io(2 * u + 2);
+        g_tl = tokens_of(u + 3);
+        segment_end(2 * u + 2);
+      }
     }
   }
   if (grp == 1) write_out();
@@ -1929,6 +1969,10 @@ void attn_plan(AttnParams& p, int64_t list_len) {
   if (ns < 1) ns = 1;
   p.n_split = static_cast<int32_t>(ns);
   p.split_len = static_cast<int32_t>(sl);
+  // MLA over bf16 rows: workgroups of 64 heads when those of 128 would leave
+  // half the CUs idle (decode)
+  p.mla_hg = 128;
+  if (p.family == ATTN_MLA && !p.kq8 && p.Hq % 64 == 0 && wgs * ns <= 128) p.mla_hg = 64;
 }
 
 size_t attn_workspace_bytes(const AttnParams& p) {
@@ -1948,11 +1992,16 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st, hipEvent_t befo
                        dim3(64 * MLA_WAVES), MLA_Q8_LDS, st, p);
   } else if (p.family == ATTN_MLA) {
     // set on every call (the same value each time, no state kept between calls)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mla_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_LDS));
+    const bool hg64 = p.mla_hg == 64;
+    const void* fn = hg64 ? reinterpret_cast<const void*>(attn_mla_kernel<true>)
+                          : reinterpret_cast<const void*>(attn_mla_kernel<false>);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(MLA_LDS));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_mla_kernel, dim3(static_cast<unsigned>(rows * p.n_split), (p.Hq + 127) / 128),
-                       dim3(64 * MLA_WAVES), MLA_LDS, st, p);
+    const dim3 grid(static_cast<unsigned>(rows * p.n_split), hg64 ? (p.Hq + 63) / 64 : (p.Hq + 127) / 128);
+    if (hg64)
+      hipLaunchKernelGGL(attn_mla_kernel<true>, grid, dim3(64 * MLA_WAVES), MLA_LDS, st, p);
+    else
+      hipLaunchKernelGGL(attn_mla_kernel<false>, grid, dim3(64 * MLA_WAVES), MLA_LDS, st, p);
   } else if (gqa_tiled(p)) {
     // the largest size any call uses, so that concurrent calls set the same value
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_tile_kernel),

@@ -124,6 +124,7 @@ struct AttnParams {
   int32_t split_len;     // stream entries per split (multiple of 32)
   int32_t family;        // ATTN_F32 / ATTN_MLA / ATTN_GQA
   int32_t kq8;           // MLA: the latent rows are q8_0 codes (int8) with f16 block scales
+  int32_t mla_hg;        // MLA (bf16 rows): heads per workgroup, 128 or 64 (0 = 128)
 };
 enum { ATTN_F32 = 0, ATTN_MLA = 1, ATTN_GQA = 2 };
 // Block-mode list length (blocks per row) the MLA kernel keeps in LDS.
