@@ -1074,9 +1074,13 @@ hipError_t launch_scores(ScoreParams p, hipStream_t st) {
   }
   const int64_t n_tiles = (p.n_units + 31) / 32;
   // Long rows: chunks of up to 32 tiles per wave; short rows spread over 4
-  // waves; fp8 decode rows (two waves per SIMD) in chunks that give about
-  // 2048 waves.
+  // waves, unless there are rows enough to fill the GPU with fewer (every
+  // wave loads and converts its row's query first: chunks then grow until
+  // about 2048 waves remain); fp8 decode rows (two waves per SIMD) in chunks
+  // that give about 2048 waves.
   int64_t ct = (n_tiles + 3) / 4;
+  const int64_t fill_rows = (rows * n_tiles + 2047) / 2048;
+  if (ct < fill_rows) ct = fill_rows < n_tiles ? fill_rows : n_tiles;
   if (ct > 32) ct = 32;
   if (p.hist != nullptr && p.k_dtype == DSA_FP8_E4M3) {
     const int64_t fill = (rows * n_tiles + 2047) / 2048;
