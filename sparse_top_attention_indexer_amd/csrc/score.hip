@@ -326,10 +326,16 @@ __global__ __launch_bounds__(256, 2) void score_mfma_kernel(ScoreParams p) {
 // (256 bytes, 2-byte keys, D = 128) keeps its 16-byte chunk c in slot
 // c ^ (r & 15), so that a wave's B-operand read (lane n: row n, chunk
 // 8 h2 + ks) is free of LDS bank conflicts.
-constexpr int SC_TILE_BYTES = 32 * 256;   // one key tile
 constexpr int SC_NBUF = 4;                      // tiles: a pair computed, a pair in flight
 constexpr int SC_MAX_TILES = 32;                // chunk_tiles bound for this kernel
-constexpr size_t SC_LDS = SC_NBUF * SC_TILE_BYTES + 4 * SC_MAX_TILES * 32 * 4 + 16;
+// 2-byte keys: 256-byte rows; f32 keys (pooled blocks): 512-byte rows, two
+// workgroups per CU
+template <int KK> struct TiledGeom {
+  static constexpr int ROW = KK == KK_F32 ? 512 : 256;   // bytes per key row
+  static constexpr int TB = 32 * ROW;                     // bytes per tile
+  static constexpr int NLD = 8 * ROW / 1024;              // 1 KB gather loads per wave and tile
+  static constexpr size_t LDS = SC_NBUF * TB + 4 * SC_MAX_TILES * 32 * 4 + 16;
+};
 
 typedef __attribute__((address_space(3))) void sc_lds_void_t;
 
@@ -339,12 +345,14 @@ __device__ __forceinline__ void sc_dma16(const void* sbase, uint32_t voff, uint3
 }
 
 template <int KK, int QK, int RB, int NQ>
-__global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(ScoreParams p) {
-  static_assert(KK == KK_BF16 || KK == KK_F16, "2-byte keys only");
+__global__ __launch_bounds__(256, NQ == 2 || KK == KK_F32 ? 2 : 3) void score_tiled_kernel(ScoreParams p) {
+  static_assert(KK == KK_BF16 || KK == KK_F16 || KK == KK_F32, "2- or 4-byte keys");
+  using G = TiledGeom<KK>;
   constexpr bool F16OP = KK == KK_F16;
+  constexpr int NK = KK == KK_F32 ? 2 : 1;   // key operands a step: f32 keys as bf16 high part + residual
   extern __shared__ __align__(16) uint8_t s_raw[];
-  uint8_t* s_kt = s_raw;                                                      // SC_NBUF tiles
-  float* s_sc = reinterpret_cast<float*>(s_raw + SC_NBUF * SC_TILE_BYTES);   // [4][chunk_tiles * 32]
+  uint8_t* s_kt = s_raw;                                                  // SC_NBUF tiles
+  float* s_sc = reinterpret_cast<float*>(s_raw + SC_NBUF * G::TB);       // [4][chunk_tiles * 32]
   int32_t* s_tend = reinterpret_cast<int32_t*>(s_sc + 4 * SC_MAX_TILES * 32);
 
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -378,27 +386,29 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   const int n_t = max(max(s_tend[0], s_tend[1]), max(s_tend[2], s_tend[3]));   // tiles of the workgroup
 
   // gather of tile T into slot T % SC_NBUF: wave w loads rows 8 w .. 8 w + 7
-  // (two 1 KB loads; lane L of load i: row 8 w + 4 i + L / 16, slot L & 15)
+  // (NLD 1 KB loads; lane L of load i: row 8 w + (1024 i + 16 L) / ROW, the
+  // 16-byte slot (16 L % ROW) / 16 of that row)
   const uint32_t kt_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((sc_lds_void_t*)s_kt));
-  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * 256;
-  // lane parts of the gather (row r = 8 w + 4 i + lane / 16 of the tile,
-  // swizzled slot) and the tile base; rows past the keys read the last row
+  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(s) * p.n_units * G::ROW;
+  // lane parts of the gather (row r of the tile, the chunk that belongs in
+  // its swizzled slot) and the tile base; rows past the keys read the last row
   const uint32_t n_units32 = static_cast<uint32_t>(p.n_units), u_begin32 = static_cast<uint32_t>(u_begin);
-  uint32_t g_r[2], g_sl[2];
+  constexpr int LPR = G::ROW / 16;   // lanes per row of a load
+  uint32_t g_r[G::NLD], g_sl[G::NLD];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t r = 8 * wid + 4 * i + (lane >> 4);
+  for (int i = 0; i < G::NLD; ++i) {
+    const uint32_t r = 8 * wid + (1024 / G::ROW) * i + lane / LPR;
     g_r[i] = r;
-    g_sl[i] = 16u * ((lane & 15) ^ (r & 15));
+    g_sl[i] = 16u * ((lane & (LPR - 1)) ^ (r & 15));
   }
   auto issue = [&](int T) __attribute__((always_inline)) {
     const uint32_t t0 = u_begin32 + 32u * static_cast<uint32_t>(T);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < G::NLD; ++i) {
       uint32_t u = t0 + g_r[i];
       u = u < n_units32 ? u : n_units32 - 1;   // past the end: any valid row, never used
-      sc_dma16(kbase, u * 256u + g_sl[i],
-               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * SC_TILE_BYTES + 1024u * (2 * wid + i)));
+      sc_dma16(kbase, u * static_cast<uint32_t>(G::ROW) + g_sl[i],
+               __builtin_amdgcn_readfirstlane(kt_lds + (T % SC_NBUF) * G::TB + 1024u * (G::NLD * wid + i)));
     }
   };
   if (n_t > 0) issue(0);
@@ -407,22 +417,34 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
   u32x4_t qa[RB][8][NQ];
   float wv[RB][16];
   if (n_t > 0) query_operands<KK, QK, RB, NQ>(p, row, n, h2, qa, wv);
-  // B operand of step ks: row n, chunk 8 h2 + ks in slot (8 h2 + ks) ^ (n & 15)
-  // = ((8 h2) ^ (n & 15)) ^ ks, so the step only flips the low 3 slot bits
-  const uint32_t b_off = n * 256u + 16u * ((8u * h2) ^ (n & 15));
+  // B operand of step ks: row n, dims 64 h2 + 8 ks .. + 7.  2-byte keys:
+  // chunk 8 h2 + ks in slot (8 h2 + ks) ^ (n & 15) = ((8 h2) ^ (n & 15)) ^ ks,
+  // so the step only flips the low 3 slot bits.  f32 keys: chunks
+  // 16 h2 + 2 ks + j (j = 0, 1) in slots 16 h2 + ((n & 15) ^ 2 ks ^ j).
+  const uint32_t b_off = KK == KK_F32 ? n * 512u + 16u * (16u * h2 + (n & 15))
+                                      : n * 256u + 16u * ((8u * h2) ^ (n & 15));
 
   auto products = [&](uint32_t kof, f32x16_t (&acc)[RB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(s_kt + (kof ^ (16u * ks)));
+      u32x4_t bh, bl;
+      if constexpr (KK == KK_F32) {
+        KeyTile<KK_F32> kt2;   // the two chunks of step ks, as key_operand reads them
+        kt2.v[2 * ks] = *reinterpret_cast<const u32x4_t*>(s_kt + (kof ^ (32u * ks)));
+        kt2.v[2 * ks + 1] = *reinterpret_cast<const u32x4_t*>(s_kt + (kof ^ (32u * ks + 16u)));
+        key_operand<KK_F32>(kt2, ks, bh, bl);
+      } else {
+        bh = *reinterpret_cast<const u32x4_t*>(s_kt + (kof ^ (16u * ks)));
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if constexpr (F16OP) {
           acc[rb] = mfma32x32x16_f16(qa[rb][ks][0], bh, acc[rb]);
         } else {
           acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bh, acc[rb]);
+          if constexpr (NK == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][0], bl, acc[rb]);
           if constexpr (NQ == 2) acc[rb] = mfma32x32x16_bf16(qa[rb][ks][NQ - 1], bh, acc[rb]);
         }
       }
@@ -452,7 +474,7 @@ __global__ __launch_bounds__(256, NQ == 2 ? 2 : 3) void score_tiled_kernel(Score
     for (int d = 0; d < 2; ++d) {
       const int Tt = T + d;
       if (Tt < t_own) {
-        uint32_t kof = (Tt % SC_NBUF) * SC_TILE_BYTES + b_off;
+        uint32_t kof = (Tt % SC_NBUF) * G::TB + b_off;
         asm volatile("" : "+v"(kof));
         f32x16_t acc0[RB];
         __builtin_amdgcn_s_setprio(1);   // the product chain first; the other waves' epilogues fill the gaps
@@ -929,8 +951,9 @@ static hipError_t launch_mfma_rb(const ScoreParams& p, dim3 grid, size_t lds, hi
 
 // the tiled prefill kernel covers 2-byte keys, n_q a multiple of 4, no histogram
 static bool scores_use_tiled(const ScoreParams& p) {
-  return (p.k_dtype == DSA_BF16 || p.k_dtype == DSA_F16) && p.n_q % 4 == 0 && p.hist == nullptr &&
-         p.chunk_tiles <= SC_MAX_TILES && p.n_units < (int64_t(1) << 24);   // 32-bit row offsets
+  return (p.k_dtype == DSA_BF16 || p.k_dtype == DSA_F16 || p.k_dtype == DSA_F32) && p.n_q % 4 == 0 &&
+         p.hist == nullptr && p.chunk_tiles <= SC_MAX_TILES &&
+         p.n_units * (p.k_dtype == DSA_F32 ? 512 : 256) < (int64_t(1) << 32);   // 32-bit row offsets
 }
 
 // the decode stream kernel covers 1- and 2-byte keys on rows with the histogram
@@ -1014,10 +1037,17 @@ template <int KK, int QK, int NQ>
 static hipError_t launch_tiled_rb(const ScoreParams& p, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(p.S) * p.n_q;
   const dim3 grid(static_cast<unsigned>((rows / 4 + 7) / 8 * 8 * p.n_chunks));
+  constexpr size_t lds = TiledGeom<KK>::LDS;
+  const void* fn = p.H <= 32 ? reinterpret_cast<const void*>(score_tiled_kernel<KK, QK, 1, NQ>)
+                             : reinterpret_cast<const void*>(score_tiled_kernel<KK, QK, 2, NQ>);
+  if (lds > 65536) {   // set on every call (the same value each time, no state kept between calls)
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
   if (p.H <= 32)
-    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 1, NQ>), grid, dim3(256), SC_LDS, st, p);
+    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 1, NQ>), grid, dim3(256), lds, st, p);
   else
-    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 2, NQ>), grid, dim3(256), SC_LDS, st, p);
+    hipLaunchKernelGGL((score_tiled_kernel<KK, QK, 2, NQ>), grid, dim3(256), lds, st, p);
   return hipGetLastError();
 }
 
@@ -1035,7 +1065,7 @@ static hipError_t launch_mfma_q(const ScoreParams& p, dim3 grid, size_t lds, hip
       return split ? launch_stream_rb<KK, 1, 2>(p, grid, st) : launch_stream_rb<KK, 1, 1>(p, grid, st);
     }
   }
-  if constexpr (KK == KK_BF16 || KK == KK_F16) {
+  if constexpr (KK == KK_BF16 || KK == KK_F16 || KK == KK_F32) {
     if (scores_use_tiled(p)) {
       if (p.q_dtype == DSA_BF16)
         return split ? launch_tiled_rb<KK, 0, 2>(p, st) : launch_tiled_rb<KK, 0, 1>(p, st);
