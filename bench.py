@@ -75,12 +75,12 @@ def score_kernel_name(wl):
     rows = wl.S * wl.n_q
     if wl.k_dtype == torch.float32 and wl.q_dtype == torch.float32:
         return "score_valu_kernel"
-    if wl.c > 1:
-        return "score_mfma_kernel"   # pooled block keys are f32
+    if wl.c > 1:   # pooled block keys are f32
+        return "score_tiled_kernel" if wl.n_q % 4 == 0 else "score_mfma_kernel"
     multiblock = n_units > 16384 or (rows < 128 and n_units > 4096)
     if multiblock and wl.k_dtype != torch.float32:
         return "score_stream_kernel"
-    if wl.k_dtype in (torch.bfloat16, torch.float16) and wl.n_q % 4 == 0:
+    if wl.k_dtype in (torch.bfloat16, torch.float16, torch.float32) and wl.n_q % 4 == 0:
         return "score_tiled_kernel"
     return "score_mfma_kernel"
 
