@@ -1563,13 +1563,19 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   // the column's multiplicity for key tile kt of block bl: 0 when its query
   // skips the tile
   const int32_t c_cb = qi * nb;   // the query's row of the multiplicity table
-  auto tile_mult = [&](int kt, int bl) __attribute__((always_inline)) -> uint32_t {
+  // In two halves, so that the table read can be issued a step before its
+  // value is used: cnt_word reads the table word, mult_of finishes.
+  auto cnt_word = [&](int bl) __attribute__((always_inline)) -> uint32_t {
+    if (nb == 0) return 0u;
+    const int blc = bl < nb ? bl : nb - 1;   // a tile past the complete blocks is every query's tail
+    return s_cnt[static_cast<uint32_t>(c_cb + blc) >> 1];
+  };
+  auto mult_of = [&](int kt, int bl, uint32_t w) __attribute__((always_inline)) -> uint32_t {
     const int t0 = kt * TILE;
     uint32_t cnt = 1u;
     if (nb > 0) {
-      const int blc = bl < nb ? bl : nb - 1;   // a tile past the complete blocks is every query's tail
-      const uint32_t at = static_cast<uint32_t>(c_cb + blc);
-      cnt = (s_cnt[at >> 1] >> (16 * (at & 1))) & 0xffffu;
+      const int blc = bl < nb ? bl : nb - 1;
+      cnt = (w >> (16 * (static_cast<uint32_t>(c_cb + blc) & 1))) & 0xffffu;
     }
     const bool vis = c_ok && t0 < c_nv;
     return vis ? (t0 >= c_tl ? 1u : cnt) : 0u;
@@ -1683,31 +1689,48 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   auto block_of = [&](int kt) __attribute__((always_inline)) -> int {
     return tpb > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(kt), tpb_m)) : kt;
   };
-  auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
-    return kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s_tiles[u])));
+  // the list entry of position u as read from LDS (a position past the list
+  // reads its last entry: such a tile gets multiplicity 0), and its tile id
+  auto tile_raw = [&](int u) __attribute__((always_inline)) -> uint32_t {
+    return s_tiles[u < n_need ? u : n_need - 1];
   };
-  if (n_need > 0) load_tile(tile_at(0), 0);
-  if (n_need > 1) load_tile(tile_at(1), 1);
+  auto tile_id = [&](uint32_t raw) __attribute__((always_inline)) -> int {
+    return kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(raw));
+  };
+  // The bookkeeping runs one pair ahead: while pair u is computed, the tile
+  // ids of pair u + 4 and the table words of pair u + 2 are read, so that no
+  // LDS round trip stands between a barrier and the step.  A pair without a
+  // second tile takes the first tile's buffer with multiplicity 0 for every
+  // column (finite scores, zero weights).
+  int ka = 0, kb_ = 0, kc = 0, kd = 0;
+  uint32_t ma = 0u, mb_ = 0u;
+  if (n_need > 0) {
+    ka = tile_id(tile_raw(0));
+    kb_ = tile_id(tile_raw(1));
+    load_tile(ka, 0);
+    if (n_need > 1) load_tile(kb_, 1);
+    ma = mult_of(ka, block_of(ka), cnt_word(block_of(ka)));
+    mb_ = n_need > 1 ? mult_of(kb_, block_of(kb_), cnt_word(block_of(kb_))) : 0u;
+    kc = tile_id(tile_raw(2));
+    kd = tile_id(tile_raw(3));
+  }
   for (int u = 0; u < n_need; u += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this pair's loads have landed
     __syncthreads();
-    if (u + 2 < n_need) load_tile(tile_at(u + 2), (u + 2) % GT_NBUF);
-    if (u + 3 < n_need) load_tile(tile_at(u + 3), (u + 3) % GT_NBUF);
-    const int ka = tile_at(u);
-    const uint32_t ma = tile_mult(ka, block_of(ka));
-    const bool aa = __ballot(ma != 0u) != 0;
-    int kb_ = ka;
-    uint32_t mb_ = 0u;
-    bool ab = false;
-    if (u + 1 < n_need) {
-      kb_ = tile_at(u + 1);
-      mb_ = tile_mult(kb_, block_of(kb_));
-      ab = __ballot(mb_ != 0u) != 0;
-    }
-    // a pair without a second tile takes the first tile's buffer with
-    // multiplicity 0 for every column (finite scores, zero weights)
+    if (u + 2 < n_need) load_tile(kc, (u + 2) % GT_NBUF);
+    if (u + 3 < n_need) load_tile(kd, (u + 3) % GT_NBUF);
+    const int blc_ = block_of(kc), bld = block_of(kd);
+    const uint32_t wc = cnt_word(blc_), wd = cnt_word(bld);
+    const uint32_t re = tile_raw(u + 4), rf = tile_raw(u + 5);
+    const bool aa = __ballot(ma != 0u) != 0, ab = __ballot(mb_ != 0u) != 0;
     const int bfa = u % GT_NBUF, bfb = u + 1 < n_need ? (u + 1) % GT_NBUF : bfa;
     if (aa || ab) step(two_t{}, {bfa, bfb}, {ka, kb_}, {ma, mb_});
+    ma = u + 2 < n_need ? mult_of(kc, blc_, wc) : 0u;
+    mb_ = u + 3 < n_need ? mult_of(kd, bld, wd) : 0u;
+    ka = kc;
+    kb_ = kd;
+    kc = tile_id(re);
+    kd = tile_id(rf);
   }
 
   // output: accumulator (db, j) holds dim 16 db + 4 q + j of column col
