@@ -1470,6 +1470,12 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   const int qi = wid * QPC + col / G;
   const bool c_ok = qi < nqt;
   const int32_t c_nv = s_nv[qi], c_tl = s_tl[qi];
+  // the smallest visible count among the wave's queries (wave-uniform): a
+  // tile that ends below it crosses no query's last visible token
+  int32_t nv_min = c_ok ? c_nv : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nv_min = min(nv_min, __shfl_xor(nv_min, o, 64));
+  nv_min = __builtin_amdgcn_readfirstlane(nv_min);
   u32x4_t qf[4];
   {
     const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((row0 + (c_ok ? qi : 0)) * p.Hq + head) * GQA_D;
@@ -1613,12 +1619,14 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int t0 = kt[i] * TILE;
-      if (__ballot(mult[i] != 0u && t0 + TILE > c_nv) != 0) {
-        const int lim = c_nv - t0 - 4 * q;   // keys j < lim (+ 16 mb) are visible
+      if (t0 + TILE > nv_min) {
+        if (__ballot(mult[i] != 0u && t0 + TILE > c_nv) != 0) {
+          const int lim = c_nv - t0 - 4 * q;   // keys j < lim (+ 16 mb) are visible
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j >= lim) s[i][0][j] = NEG_INF;
-          if (16 + j >= lim) s[i][1][j] = NEG_INF;
+          for (int j = 0; j < 4; ++j) {
+            if (j >= lim) s[i][0][j] = NEG_INF;
+            if (16 + j >= lim) s[i][1][j] = NEG_INF;
+          }
         }
       }
       const float t = vmax3(vmax3(s[i][0][0], s[i][0][1], s[i][0][2]), vmax3(s[i][0][3], s[i][1][0], s[i][1][1]),
@@ -1633,12 +1641,23 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
     m_run = (first || grow) ? tmax : m_run;
     const float mc = m_run == NEG_INF ? 0.f : m_run * c2;
     // the multiplicity scales the weights: offset log2(mult), zero -> +inf
+    // (a listing count above 1 comes only from a list that names a block
+    // twice: a branch of its own, kept out of the common path)
     float mo[2];
     float mo_min = __builtin_inff();
 #pragma unroll
+    for (int i = 0; i < N; ++i) mo[i] = mc;
+    bool rep = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) rep = rep || mult[i] > 1u;
+    if (__ballot(rep) != 0) {
+      asm volatile("" ::: "memory");   // not speculated into the common path
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        mo[i] -= __builtin_amdgcn_logf(static_cast<float>(mult[i] > 1u ? mult[i] : 1u));
+    }
+#pragma unroll
     for (int i = 0; i < N; ++i) {
-      mo[i] = mc;
-      if (__ballot(mult[i] > 1u) != 0) mo[i] -= __builtin_amdgcn_logf(static_cast<float>(mult[i] > 1u ? mult[i] : 1u));
       mo[i] = mult[i] != 0u ? mo[i] : __builtin_inff();
       mo_min = fminf(mo_min, mo[i]);
     }
