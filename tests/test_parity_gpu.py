@@ -381,6 +381,14 @@ MLA_SHAPE_CASES = {
     "mla_144_heads": lambda: inputs.Workload(
         "mla144", 1, 40, 700, 660, 32, 128, torch.bfloat16, torch.bfloat16, "normal", 0.2, 300, 1, 0, False,
         "mla", 144, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=95),
+    # decode rows that take workgroups of 64 heads (waves 0, 1, 6, 7 hold the
+    # heads, the other four only gather): one head group, and three
+    "mla_64_heads_decode": lambda: inputs.Workload(
+        "mla64", 5, 1, 3001, 3000, 32, 128, torch.bfloat16, torch.bfloat16, "normal", 0.2, 1024, 1, 1, False,
+        "mla", 64, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=97),
+    "mla_192_heads_decode": lambda: inputs.Workload(
+        "mla192", 3, 1, 2500, 2499, 32, 128, torch.bfloat16, torch.bfloat16, "normal", 0.2, 1024, 1, 0, False,
+        "mla", 192, 1, 576, 512, torch.bfloat16, 576 ** -0.5, seed=98),
     # block mode: 16-token blocks plus the tail
     "mla_block_mode": lambda: inputs.Workload(
         "mlablk", 1, 60, 1000, 940, 16, 128, torch.bfloat16, torch.bfloat16, "normal", 0.25, 256, 16, 0, False,
@@ -404,7 +412,8 @@ def test_mla_head_counts_and_block_mode(case):
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("case", ["mla_48_heads_split", "mla_144_heads"])
+@pytest.mark.parametrize("case", ["mla_48_heads_split", "mla_144_heads", "mla_64_heads_decode",
+                                  "mla_192_heads_decode"])
 def test_mla_writes_only_its_output(case):
     # Waves without heads (48 heads: waves 3..7 of every workgroup; 144: waves
     # 1..7 of the second head block) run their products on head 0's query and
