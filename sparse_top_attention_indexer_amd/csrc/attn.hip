@@ -441,12 +441,16 @@ __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams 
         if (!((lm >> (16 + j)) & 1u)) s1[j] = NEG_INF;
       }
     }
-    float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    tmax = quad_max(tmax);
+    float tmax = vmax3(vmax3(s0[0], s0[1], s0[2]), vmax3(s0[3], s1[0], s1[1]), vmax3(s1[2], s1[3], NEG_INF));
+    tmax = quad_vmax(tmax);
     const bool first = m_run == NEG_INF;
     const bool grow = !first && (tmax - m_run) * c2 > 8.f;
-    const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
-    const float alpha = grow ? a : 1.f;
+    float alpha = 1.f;   // the rescale factor, computed only when some head's max moves
+    if (__ballot(grow) != 0) {
+      asm volatile("" ::: "memory");   // not speculated into the common path
+      const float a = __builtin_amdgcn_exp2f((m_run - tmax) * c2);
+      alpha = grow ? a : 1.f;
+    }
     m_run = (first || grow) ? tmax : m_run;
     mb = m_run == NEG_INF ? 0.f : m_run * c2;   // an all-dead prefix gives zero weights
     const float xmax = __builtin_amdgcn_exp2f(fmaf(tmax, c2, -mb));   // the head's largest weight in the tile
