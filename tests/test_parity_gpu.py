@@ -143,6 +143,14 @@ SCORE_CASES = {
     "f32_keys_mfma": lambda: inputs.Workload(
         "f32k", 1, 9, 333, 320, 16, 128, torch.bfloat16, torch.float32, "normal", 0.25, 64, 1, 0,
         False, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=79),
+    # f32 keys on the LDS-tiled kernel (rows in groups of 4): 64 heads (two
+    # head blocks), and 40 heads with an f16 query split in two operands
+    "f32_keys_tiled_64_heads": lambda: inputs.Workload(
+        "f32kt", 2, 12, 1200, 1180, 64, 128, torch.bfloat16, torch.float32, "normal", 0.125, 64, 1, 0,
+        False, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=82),
+    "f32_keys_tiled_split_q": lambda: inputs.Workload(
+        "f32kts", 1, 8, 700, 690, 40, 128, torch.float16, torch.float32, "normal", 0.2, 64, 1, 0,
+        False, "gqa", 8, 1, 128, 128, torch.bfloat16, 0.1, seed=83),
 }
 
 
