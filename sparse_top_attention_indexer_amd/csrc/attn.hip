@@ -209,7 +209,9 @@ __device__ __forceinline__ float quad_sum(float x) {
 // one wave's score products overlap the other wave's exponentials and PV
 // products.  Tiles are gathered with direct global -> LDS loads two
 // segments ahead (three tile buffers).  Token ids of the stream sit in an LDS
-// ring of 32 tiles, refilled 16 tiles ahead.
+// ring of 32 tiles, refilled 16 tiles ahead.  HG64: a workgroup of 64 heads
+// (few rows: the decode split), whose heads sit on waves 0, 1, 6 and 7, one
+// computing wave per SIMD; the other four gather and synchronise only.
 template <bool HG64>
 __global__ __launch_bounds__(64 * MLA_WAVES, 1) void attn_mla_kernel(AttnParams p) {
   constexpr int NW = MLA_WAVES;
