@@ -353,7 +353,9 @@ typedef struct {
   int32_t* idx_out;       /* optional [S, n_q, top_k / c]                       */
   float* scores_out;      /* optional [S, n_q, n_units] (n_units = n_kv / c in block mode) */
   /* optional timing: NULL, or DSA_N_PHASE_EVENTS hipEvent_t handles recorded
-   * on the stream at the phase boundaries */
+   * on the stream at the phase boundaries (before the first launch, after
+   * the scores, after the top-k, before the split merge, after the last
+   * launch); a NULL entry is not recorded */
   void* const* phase_events;
   const void* kv_scale;   /* as in dsa_attn_desc                                */
 } dsa_forward_desc;

@@ -372,7 +372,7 @@ def forward(Q, K, V, q_idx, k_idx, w, top_k: int, compress_ratio: int, q_pos, *,
                   if return_scores else None)
     events_arr = None
     if phase_events is not None:
-        events_arr = (ctypes.c_void_p * 5)(*[e.handle.value for e in phase_events])
+        events_arr = (ctypes.c_void_p * 5)(*[None if e is None else e.handle.value for e in phase_events])
     d = _forward_desc(Q, K, V, q_idx, k_idx, w, top_k, c, q_pos, k_scale, n_sink, scale, hadamard_q,
                       kv_len, out, idx_out, scores_out, events_arr, kv_scale)
     nbytes = int(lib().dsa_forward_workspace_bytes(ctypes.byref(d)))

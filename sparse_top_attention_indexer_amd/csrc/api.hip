@@ -495,8 +495,8 @@ int dsa_forward(const dsa_forward_desc* d, void* workspace, size_t workspace_byt
   do {                                     \
     if ((e = (x)) != hipSuccess) return DSA_ERR_HIP; \
   } while (0)
-  auto mark = [&](int i) -> hipError_t {
-    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  auto mark = [&](int i) -> hipError_t {   // a null entry is skipped
+    return ev && ev[i] ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   };
   int32_t* idx = d->idx_out ? d->idx_out : reinterpret_cast<int32_t*>(ws + f.off_idx);
   DSA_TRY(mark(0));
