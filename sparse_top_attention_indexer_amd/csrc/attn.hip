@@ -1303,18 +1303,20 @@ __global__ __launch_bounds__(64, 2) void attn_gqa_kernel(AttnParams p) {
 
 // ===================================================== GQA query tiles ==
 
-// Workgroup of the query-tile kernel: GT_WAVES waves, each with two groups
-// of 16 MFMA columns; a column is a (query, head) pair of one KV group, so a
-// workgroup takes 128 / G consecutive queries of one sequence (G = heads per
-// group, a divisor of 16).
-constexpr int GT_WAVES = 8;
-constexpr int GT_NL = 8 / GT_WAVES;          // 1 KB K (and V) loads per wave and tile
+// Workgroup of the query-tile kernel: GT_WAVES waves, each with one group of
+// 16 MFMA columns; a column is a (query, head) pair of one KV group, so a
+// workgroup takes 256 / G consecutive queries of one sequence (G = heads per
+// group, a divisor of 16).  One workgroup fills a CU (1024 threads, up to
+// 160 KB of LDS).
+constexpr int GT_WAVES = 16;
 constexpr int GT_KV = TILE * GQA_D * 2;      // K (or V) rows of one tile of one group (8 KB)
 constexpr int GT_BUF = 2 * GT_KV;            // one tile: K rows, then V rows
-constexpr int GT_NBUF = 4;                   // a pair computed, a pair being loaded
-constexpr int GT_QMAX = GT_WAVES * 16;   // queries of a workgroup (G = 1)
+constexpr int GT_RING = 4;                   // pairs of tiles resident in LDS
+constexpr int GT_NBUF = 2 * GT_RING;         // tile buffers
+constexpr int GT_JOBS = 2;                   // load jobs of a pair: one tile each (16 KB: K rows, then V rows)
+constexpr int GT_QMAX = GT_WAVES * 16;       // queries of a workgroup (G = 1)
 constexpr int GT_MAX_TILES = 2048;           // key tiles of one split
-constexpr int GT_MAX_CNT = 16384;            // (query, block) multiplicities in LDS (u16)
+constexpr int GT_MAX_CNT = 12288;            // (query, block) multiplicities in LDS (u16)
 
 static int gt_queries(const AttnParams& p) { return GT_WAVES * 16 / (p.Hq / p.Hkv); }
 static int64_t gt_blocks(const AttnParams& p) { return p.idx ? p.n_kv / p.c : 0; }
@@ -1334,9 +1336,10 @@ bool gqa_tiled(const AttnParams& p) {
 
 static size_t gt_lds_bytes(const AttnParams& p) {
   const size_t cnt = (static_cast<size_t>(gt_queries(p)) * gt_blocks(p) + 1) / 2 * 4;
-  return GT_NBUF * GT_BUF + 64 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + cnt;
+  return GT_NBUF * GT_BUF + 128 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + cnt;
 }
-static constexpr size_t GT_LDS_MAX = GT_NBUF * GT_BUF + 64 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + GT_MAX_CNT * 2;
+static constexpr size_t GT_LDS_MAX = GT_NBUF * GT_BUF + 128 + 2 * GT_QMAX * 4 + GT_MAX_TILES * 2 + GT_MAX_CNT * 2;
+static_assert(GT_LDS_MAX <= 160 * 1024, "query-tile kernel LDS");
 
 // Workgroups: (sequence, split, query tile) units times the KV groups; as in
 // gqa_grid, workgroup b runs on XCD b % 8 and takes its group from b % 8
@@ -1353,8 +1356,9 @@ static int64_t gt_grid(const AttnParams& p) {
 // tokens is attention over all positions with the others weighted zero: the
 // workgroup walks the key positions of its split in tiles of 32, skipping
 // tiles that no query of the tile attends to, and each tile's K and V rows
-// go once into LDS (direct global -> LDS loads, two tiles ahead), where all
-// 128 columns read them.  A query's weight for a token is its multiplicity:
+// go once into LDS (direct global -> LDS loads into a ring of four pairs of
+// tiles), where all 256 columns read them.  A query's weight for a token is
+// its multiplicity:
 // in block mode the number of times its idx row lists the token's block
 // (live entries: 0 <= b < n_cb), and 1 for the incomplete tail n_cb c ..
 // n_vis - 1; in dense mode 1 for every visible token.  A list that names a
@@ -1362,8 +1366,9 @@ static int64_t gt_grid(const AttnParams& p) {
 // gathered stream do; the summation runs in position order instead of list
 // order.  A tile lies in one block (32 | c), so its multiplicity per query
 // is one count, read from an LDS table built from the idx rows.
-// Each wave holds 16 columns (query, head) and takes the tiles in pairs,
-// both tiles of a pair in one step:
+// Each wave holds 16 columns (query, head) and takes the tiles in pairs, at
+// its own pace (no workgroup barrier in the loop), both tiles of a pair in
+// one step:
 //   scores  S^T (32 keys x 16 columns) = K_tile . Q^T per tile, 16x16x32
 //           MFMAs, Q in registers
 //   softmax per column over the 64 keys of the pair (attn_mla_kernel's lazy
@@ -1371,7 +1376,9 @@ static int64_t gt_grid(const AttnParams& p) {
 //   PV      O^T (128 dims x 16 columns) += V^T . P^T per tile, V^T fragments
 //           through the transposing LDS read
 // A wave whose columns all skip both tiles of a pair skips the step; a tile
-// of the step that every column skips gets zero weights.
+// of the step that every column skips gets zero weights.  The step runs at a
+// wave priority that grows with the number of waves already past its pair,
+// so that the waves the ring waits for issue first.
 // K row t keeps 16-byte chunk c of its 256 bytes in slot c ^ (t & 15) and
 // V row t its 32-byte dim block b in slot b ^ (t & 7) (attn_gqa_kernel's V
 // layout): the fragment reads are free of bank conflicts.
@@ -1380,7 +1387,8 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   extern __shared__ __align__(16) uint8_t s_raw[];
   uint8_t* s_kv = s_raw;                                                          // GT_NBUF tiles
   uint32_t* s_scr = reinterpret_cast<uint32_t*>(s_raw + GT_NBUF * GT_BUF);      // 16 words
-  int32_t* s_nv = reinterpret_cast<int32_t*>(s_scr + 16);                        // n_vis per query
+  uint32_t* s_sync = s_scr + 16;                                                 // ring counters, 16 words
+  int32_t* s_nv = reinterpret_cast<int32_t*>(s_sync + 16);                       // n_vis per query
   int32_t* s_tl = s_nv + GT_QMAX;                                                // first tail token per query
   uint16_t* s_tiles = reinterpret_cast<uint16_t*>(s_tl + GT_QMAX);               // needed tiles of the split
   uint32_t* s_cnt = reinterpret_cast<uint32_t*>(s_tiles + GT_MAX_TILES);         // multiplicities, u16 pairs
@@ -1421,6 +1429,7 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   }
   const int cnt_words = (QT * nb + 1) / 2;
   for (int i = tid; i < cnt_words; i += NT) s_cnt[i] = 0u;
+  if (tid < 16) s_sync[tid] = 0u;
   __syncthreads();
   auto count = [&](int qi, int bl) __attribute__((always_inline)) -> uint32_t {
     const uint32_t at = static_cast<uint32_t>(qi * nb + bl);
@@ -1490,41 +1499,13 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
       qf[ks] = c_ok ? *reinterpret_cast<const u32x4_t*>(qr + 32 * ks + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // tile loads: wave w, load i copies tile rows 4 (2 w + i) .. + 3 (1 KB of
-  // K, then of V); lane L fills slot L % 16 of row 4 (2 w + i) + L / 16.
+  // K and V rows of the tiles: K row t keeps 16-byte chunk c of its 256 bytes
+  // in slot c ^ (t & 15), V row t its 32-byte dim block b in slot b ^ (t & 7).
   // Rows no query of the tile sees read row 0 (zero weight).
   const uint32_t kv_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)s_kv));
   const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) + s * p.k_seq + g * p.k_head);
   const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + s * p.v_seq + g * p.v_head);
   const uint32_t kpitch = static_cast<uint32_t>(p.k_tok) * 2u, vpitch = static_cast<uint32_t>(p.v_tok) * 2u;
-  // lane offsets within a tile (rows r = 4 (2 w + i) + lane / 16) and the
-  // same rows' offsets for row 0 (rows past every query's view)
-  uint32_t k_lo[GT_NL], v_lo[GT_NL], k_r0[GT_NL], v_r0[GT_NL];
-#pragma unroll
-  for (int i = 0; i < GT_NL; ++i) {
-    const uint32_t r = 4 * (GT_NL * wid + i) + (lane >> 4), sl = lane & 15;
-    k_r0[i] = 16u * (sl ^ (r & 15));
-    v_r0[i] = 16u * ((2u * ((sl >> 1) ^ (r & 7))) | (sl & 1u));
-    k_lo[i] = r * kpitch + k_r0[i];
-    v_lo[i] = r * vpitch + v_r0[i];
-  }
-  auto load_tile = [&](int kt, int bf) __attribute__((always_inline)) {
-    const int t0 = kt * TILE;
-    const bool whole = t0 + TILE <= vmax;   // wave-uniform
-    const uint32_t kb0 = static_cast<uint32_t>(t0) * kpitch, vb0 = static_cast<uint32_t>(t0) * vpitch;
-#pragma unroll
-    for (int i = 0; i < GT_NL; ++i) {
-      uint32_t ko = kb0 + k_lo[i], vo = vb0 + v_lo[i];
-      if (!whole) {
-        const bool in = t0 + 4 * (GT_NL * wid + i) + (lane >> 4) < vmax;
-        ko = in ? ko : k_r0[i];
-        vo = in ? vo : v_r0[i];
-      }
-      const uint32_t lb = kv_lds + static_cast<uint32_t>(bf * GT_BUF) + 1024u * (GT_NL * wid + i);
-      dma16(kb, ko, __builtin_amdgcn_readfirstlane(lb));
-      dma16(vb, vo, __builtin_amdgcn_readfirstlane(lb + GT_KV));
-    }
-  };
 
   // o[db], db < 8: dims 16 db + 4 q + j of column col (O^T); o[8]: the
   // column's normaliser in every register, as the product of the weights
@@ -1597,10 +1578,16 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   // multiplicities mult) that some column of the wave attends to: the scores
   // of all N tiles, one running-max update and one residual decision, then
   // the value products of the N tiles in position order.
+  // wave priority lv (0..3; s_setprio takes an immediate)
+  auto set_prio = [](int lv) __attribute__((always_inline)) {
+    if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+    else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
   auto step = [&](auto n_t, const int (&bf)[2], const int (&kt)[2], const uint32_t (&mult)[2])
                   __attribute__((always_inline)) {
     constexpr int N = decltype(n_t)::value;
-    __builtin_amdgcn_s_setprio(2);   // the score chain and softmax first; other waves' products fill the gaps
     // reg j of s[i][mb]: key 32 kt[i] + 16 mb + 4 q + j of column col
     f32x4_t s[2][2];
     uint32_t kt_off[2];
@@ -1695,18 +1682,96 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
 #pragma unroll
       for (int db = 0; db < 9; ++db) o[db] *= alpha;
     }
-    __builtin_amdgcn_s_setprio(0);
     pv(n_t, bf, ph);
     if (lo) pv(n_t, bf, pl);
   };
   using two_t = std::integral_constant<int, 2>;
 
-  // pipeline over pairs of tiles: the loads of pair u + 2, u + 3 run while
-  // pair u, u + 1 is computed; the barrier before them (into the buffers of
-  // pair u - 2) also ends every wave's reads of those buffers.  Tile and
-  // block ids are wave-uniform (scalar registers).  A wave attending to both
-  // tiles of a pair takes them in one step (the two tiles of a block of 64
-  // share every query's multiplicity), else the one it attends to.
+  // The tiles go through a ring of GT_RING pairs in LDS, and the waves do
+  // not meet at barriers: each wave walks the pairs at its own pace and
+  // computes only those its columns attend to, so a pair costs the waves that
+  // compute it, not the slowest wave of the workgroup.  Words of s_sync:
+  //   [i]            releases of ring slot i, over all its pairs: a wave
+  //                  releases pair u when done with it (or at once if it
+  //                  skips it); pair u + GT_RING may load into the slot once
+  //                  all GT_WAVES waves released pair u
+  //   [GT_RING + i]  load jobs of slot i landed, over all its pairs
+  //   [8]            the next load job to claim (job j: pair j / GT_JOBS)
+  // A wave that waits (for a slot or for a pair's loads) claims load jobs of
+  // pairs whose slot is free, issues them, waits for them and counts them.
+  // A wave enters pair u only once the slot holds pair u's generation (all
+  // waves released pair u - GT_RING), so the counts of one slot never mix
+  // generations; every pair has a wave that computes it (its tiles are
+  // needed), and that wave releases it only after its loads landed.  The
+  // slowest wave can always claim and load what it waits for itself, so
+  // every wait ends; a wait is still bounded by an iteration limit.
+  const int n_pairs = (n_need + 1) / 2;
+  constexpr uint32_t NWV = GT_WAVES;
+  constexpr int SPIN_MAX = 1 << 16;
+  auto sync_ld = [&](int i) __attribute__((always_inline)) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(&s_sync[i], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+  };
+  // load job j: tile j % 2 of pair j / 2, K rows then V rows in 1 KB loads;
+  // load l of a part takes rows 4 l .. 4 l + 3, lane L slot L % 16 of row
+  // 4 l + L / 16
+  auto issue_job = [&](uint32_t j) __attribute__((always_inline)) {
+    const int pj = static_cast<int>(j / GT_JOBS), ti = static_cast<int>(j % GT_JOBS);
+    const int e = 2 * pj + ti;
+    const int kt = kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(s_tiles[e < n_need ? e : n_need - 1]));
+    const int t0 = kt * TILE;
+    const uint32_t lb0 = kv_lds + static_cast<uint32_t>((2 * (pj % GT_RING) + ti) * GT_BUF);
+    const uint32_t sl16 = lane & 15;
+    const bool whole = t0 + TILE <= vmax;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const uint32_t r = 4u * l + (lane >> 4);
+      const uint32_t rk = 16u * (sl16 ^ (r & 15)), rv = 16u * ((2u * ((sl16 >> 1) ^ (r & 7))) | (sl16 & 1u));
+      uint32_t ko = (static_cast<uint32_t>(t0) + r) * kpitch + rk, vo = (static_cast<uint32_t>(t0) + r) * vpitch + rv;
+      if (!whole) {
+        const bool in = t0 + static_cast<int>(r) < vmax;
+        ko = in ? ko : rk;
+        vo = in ? vo : rv;
+      }
+      dma16(kb, ko, __builtin_amdgcn_readfirstlane(lb0 + 1024u * l));
+      dma16(vb, vo, __builtin_amdgcn_readfirstlane(lb0 + GT_KV + 1024u * l));
+    }
+  };
+  // claims one load job whose slot is free, loads it and counts it; false
+  // when there is none
+  auto try_claim = [&]() __attribute__((always_inline)) -> bool {
+    uint32_t job = 0xffffffffu;
+    if (lane == 0) {
+      uint32_t j = __hip_atomic_load(&s_sync[8], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (;;) {
+        const uint32_t pj = j / GT_JOBS;
+        if (pj >= static_cast<uint32_t>(n_pairs)) break;
+        if (pj >= GT_RING && __hip_atomic_load(&s_sync[pj % GT_RING], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                                 NWV * (pj / GT_RING))
+          break;
+        uint32_t exp = j;
+        if (__hip_atomic_compare_exchange_strong(&s_sync[8], &exp, j + 1, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP)) {
+          job = j;
+          break;
+        }
+        j = exp;
+      }
+    }
+    job = __builtin_amdgcn_readfirstlane(job);
+    if (job == 0xffffffffu) return false;
+    issue_job(job);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the job's rows are in LDS
+    if (lane == 0)
+      __hip_atomic_fetch_add(&s_sync[GT_RING + (job / GT_JOBS) % GT_RING], 1u, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    return true;
+  };
+  auto wait_for = [&](int i, uint32_t target) __attribute__((always_inline)) {
+    for (int it = 0; it < SPIN_MAX && sync_ld(i) < target; ++it)
+      if (!try_claim()) __builtin_amdgcn_s_sleep(1);
+  };
+
   const int tpb = blk ? p.c / TILE : 1;   // tiles per block
   // kt / tpb for kt < 2^16 as the high word of kt * (floor(2^32 / tpb) + 1):
   // the product overshoots kt / tpb by less than 2^-16 < 1 / tpb
@@ -1714,44 +1779,48 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
   auto block_of = [&](int kt) __attribute__((always_inline)) -> int {
     return tpb > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(kt), tpb_m)) : kt;
   };
-  // the list entry of position u as read from LDS (a position past the list
+  // the list entry of position e as read from LDS (a position past the list
   // reads its last entry: such a tile gets multiplicity 0), and its tile id
-  auto tile_raw = [&](int u) __attribute__((always_inline)) -> uint32_t {
-    return s_tiles[u < n_need ? u : n_need - 1];
+  auto tile_raw = [&](int e) __attribute__((always_inline)) -> uint32_t {
+    return s_tiles[e < n_need ? e : n_need - 1];
   };
   auto tile_id = [&](uint32_t raw) __attribute__((always_inline)) -> int {
     return kt0 + static_cast<int>(__builtin_amdgcn_readfirstlane(raw));
   };
-  // The bookkeeping runs one pair ahead: while pair u is computed, the tile
-  // ids of pair u + 4 and the table words of pair u + 2 are read, so that no
-  // LDS round trip stands between a barrier and the step.  A pair without a
-  // second tile takes the first tile's buffer with multiplicity 0 for every
-  // column (finite scores, zero weights).
+  // The bookkeeping runs ahead: while pair u is computed, the table words of
+  // pair u + 1 and the tile ids of pair u + 2 are read.  A pair without a
+  // second tile loads the first tile's rows again and gives that tile
+  // multiplicity 0 for every column (finite scores, zero weights).
   int ka = 0, kb_ = 0, kc = 0, kd = 0;
   uint32_t ma = 0u, mb_ = 0u;
   if (n_need > 0) {
     ka = tile_id(tile_raw(0));
     kb_ = tile_id(tile_raw(1));
-    load_tile(ka, 0);
-    if (n_need > 1) load_tile(kb_, 1);
     ma = mult_of(ka, block_of(ka), cnt_word(block_of(ka)));
     mb_ = n_need > 1 ? mult_of(kb_, block_of(kb_), cnt_word(block_of(kb_))) : 0u;
     kc = tile_id(tile_raw(2));
     kd = tile_id(tile_raw(3));
   }
-  for (int u = 0; u < n_need; u += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this pair's loads have landed
-    __syncthreads();
-    if (u + 2 < n_need) load_tile(kc, (u + 2) % GT_NBUF);
-    if (u + 3 < n_need) load_tile(kd, (u + 3) % GT_NBUF);
+  for (int u = 0; u < n_pairs; ++u) {
+    const int sl = u % GT_RING;
+    const uint32_t gen = static_cast<uint32_t>(u / GT_RING);
     const int blc_ = block_of(kc), bld = block_of(kd);
     const uint32_t wc = cnt_word(blc_), wd = cnt_word(bld);
-    const uint32_t re = tile_raw(u + 4), rf = tile_raw(u + 5);
-    const bool aa = __ballot(ma != 0u) != 0, ab = __ballot(mb_ != 0u) != 0;
-    const int bfa = u % GT_NBUF, bfb = u + 1 < n_need ? (u + 1) % GT_NBUF : bfa;
-    if (aa || ab) step(two_t{}, {bfa, bfb}, {ka, kb_}, {ma, mb_});
-    ma = u + 2 < n_need ? mult_of(kc, blc_, wc) : 0u;
-    mb_ = u + 3 < n_need ? mult_of(kd, bld, wd) : 0u;
+    const uint32_t re = tile_raw(2 * u + 4), rf = tile_raw(2 * u + 5);
+    const bool act = __ballot(ma != 0u || mb_ != 0u) != 0;
+    if (u >= GT_RING) wait_for(sl, NWV * gen);   // the slot holds pair u's generation
+    if (act) {
+      wait_for(GT_RING + sl, GT_JOBS * (gen + 1));   // pair u's rows have landed
+      // the more waves are past pair u, the higher this wave's priority
+      const int lv = static_cast<int>((sync_ld(sl) - NWV * gen) / (NWV / 4));
+      set_prio(lv);
+      step(two_t{}, {2 * sl, 2 * sl + 1}, {ka, kb_}, {ma, mb_});
+      __builtin_amdgcn_s_setprio(0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of the slot are done
+    if (lane == 0) __hip_atomic_fetch_add(&s_sync[sl], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ma = 2 * u + 2 < n_need ? mult_of(kc, blc_, wc) : 0u;
+    mb_ = 2 * u + 3 < n_need ? mult_of(kd, bld, wd) : 0u;
     ka = kc;
     kb_ = kd;
     kc = tile_id(re);
@@ -1975,10 +2044,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 
 void attn_plan(AttnParams& p, int64_t list_len) {
   if (gqa_tiled(p)) {
-    // splits of the key positions: two workgroups per CU, at least 16 tiles
+    // splits of the key positions: one workgroup per CU, at least 16 tiles
     // and at most GT_MAX_TILES tiles a split
     const int64_t wgs = static_cast<int64_t>(p.S) * ((p.n_q + gt_queries(p) - 1) / gt_queries(p)) * p.Hkv;
-    int64_t ns = wgs < 512 ? (512 + wgs - 1) / wgs : 1;
+    int64_t ns = wgs < 256 ? (256 + wgs - 1) / wgs : 1;
     const int64_t max_ns = (p.n_kv + 16 * TILE - 1) / (16 * TILE);
     if (ns > max_ns) ns = max_ns;
     const int64_t min_ns = (p.n_kv + int64_t(GT_MAX_TILES) * TILE - 1) / (int64_t(GT_MAX_TILES) * TILE);
