@@ -798,3 +798,35 @@ def test_gqa_query_tiles_block_sizes(c):
         worst = max(worst, float(np.abs(got - ref).max()))
     print(f"gqa query tiles, blocks of {c}: max |O - oracle| {worst:.2e}")
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (16, 1)])
+def test_gqa_query_tiles_group_sizes(hq, hkv):
+    # the query-tile GQA kernel at 1, 2, 4 and 16 heads per KV group (256, 128,
+    # 64 and 16 queries a workgroup), dense and in block mode with random
+    # block lists: ragged query tiles, two sequences of different stored
+    # lengths, and ~45 pairs of key tiles a workgroup, so that the LDS ring of
+    # four pairs is reused many times while the waves run at their own pace.
+    wl = replace(inputs.mini(4), name="qsa_groups", S=2, n_q=300, n_kv=2900, q_pos0=2600, c=64, top_k=16 * 64,
+                 Hq=hq, Hkv=hkv)
+    x = inputs.generate(wl, seed=300 + 10 * hq + hkv)
+    x["kv_len"] = torch.tensor([2900, 2750], dtype=torch.int32)
+    d = dev(x)
+    qp, kv = x["q_pos"].numpy(), x["kv_len"].numpy()
+    rng = np.random.default_rng(10 * hq + hkv)
+    idx = np.full((wl.S, wl.n_q, 16), -1, np.int64)
+    for s in range(wl.S):
+        for i in range(wl.n_q):
+            n_cb = O.visible_tokens(int(qp[s, i]), int(kv[s])) // wl.c
+            pick = rng.choice(n_cb, size=min(15, n_cb), replace=False)
+            idx[s, i, 1:1 + pick.size] = pick
+    rows = _rows_sample(wl, n=40, seed=hq + hkv)
+    worst = {}
+    for name, sel in (("dense", None), ("blocks", idx)):
+        got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"],
+                              None if sel is None else torch.from_numpy(sel.astype(np.int32)).to(DEV),
+                              c=wl.c, kv_len=d["kv_len"], scale=wl.scale).cpu().double().numpy()
+        ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), sel, qp, kv, wl.c, wl.scale, rows=rows)
+        worst[name] = max(float(np.abs(got[s, i] - ref[s, i]).max()) for s, i in rows)
+    print(f"gqa query tiles, {hq // hkv} heads a group: max |O - oracle| {worst}")
+    assert max(worst.values()) <= 2e-2
