@@ -1827,17 +1827,22 @@ __global__ __launch_bounds__(64 * GT_WAVES, 4) void attn_gqa_tile_kernel(AttnPar
     kd = tile_id(rf);
   }
 
-  // output: accumulator (db, j) holds dim 16 db + 4 q + j of column col
-  if (c_ok) {
-    const int64_t row = row0 + qi;
+  // output: accumulator (db, j) holds dim 16 db + 4 q + j of column col.
+  // The column's query and head are derived again from the lane id (opaque
+  // to the compiler), so that no 64-bit index stays live across the loop.
+  int lid = lane;
+  asm volatile("" : "+v"(lid));
+  const int qi_o = wid * QPC + (lid & 15) / G, head_o = g * G + (lid & 15) % G;
+  if (qi_o < nqt) {
+    const int64_t row = row0 + qi_o;
     if (p.n_split == 1) {
       const float inv = o[8][0] > 0.f ? 1.f / o[8][0] : 0.f;
-      const int64_t ob = (row * p.Hq + head) * GQA_D + 4 * q;
+      const int64_t ob = (row * p.Hq + head_o) * GQA_D + 4 * q;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
         store4(p.out, p.o_dtype, ob + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
     } else {
-      float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head) * part_width(GQA_D);
+      float* pp = p.part + ((row * p.n_split + sp) * p.Hq + head_o) * part_width(GQA_D);
 #pragma unroll
       for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pp + 16 * db + 4 * q) = o[db];
       if (q == 0) {
