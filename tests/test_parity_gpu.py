@@ -830,3 +830,31 @@ def test_gqa_query_tiles_group_sizes(hq, hkv):
         worst[name] = max(float(np.abs(got[s, i] - ref[s, i]).max()) for s, i in rows)
     print(f"gqa query tiles, {hq // hkv} heads a group: max |O - oracle| {worst}")
     assert max(worst.values()) <= 2e-2
+
+
+@pytest.mark.parametrize("n_kv", [20, 40, 100])
+def test_gqa_query_tiles_short_streams(n_kv):
+    # the query-tile GQA kernel on streams of one to four key tiles (one or
+    # two pairs: the ring never wraps, and an odd tile count leaves the last
+    # pair half empty), dense and in block mode, with causal queries from
+    # position 0; one sequence's block lists are all dead, so its queries
+    # attend to their incomplete tails only.
+    wl = replace(inputs.mini(4), name="qsa_short", S=2, n_q=40, n_kv=n_kv, q_pos0=0, c=32, top_k=4 * 32)
+    x = inputs.generate(wl, seed=400 + n_kv)
+    d = dev(x)
+    qp = x["q_pos"].numpy()
+    kv = np.full(wl.S, n_kv, np.int64)
+    idx = np.full((wl.S, wl.n_q, 4), -1, np.int64)
+    rng = np.random.default_rng(n_kv)
+    for i in range(wl.n_q):
+        n_cb = O.visible_tokens(int(qp[0, i]), n_kv) // wl.c
+        if n_cb:
+            idx[0, i, :min(2, n_cb)] = rng.choice(n_cb, size=min(2, n_cb), replace=False)
+    for name, sel in (("dense", None), ("blocks", idx)):
+        got = dsa.sparse_attn(d["Q"], d["K"], d["V"], d["q_pos"],
+                              None if sel is None else torch.from_numpy(sel.astype(np.int32)).to(DEV),
+                              c=wl.c, scale=wl.scale).cpu().double().numpy()
+        ref = O.sparse_attention(f64(x["Q"]), f64(x["K"]), f64(x["V"]), sel, qp, kv, wl.c, wl.scale)
+        err = float(np.nanmax(np.abs(got - np.nan_to_num(ref))))
+        print(f"gqa query tiles, {n_kv} keys, {name}: max |O - oracle| {err:.2e}")
+        assert err <= 2e-2
